@@ -1,0 +1,357 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE layer hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
+
+A step is one pass of the whole path -- moe_topk_softmax -> moe_route_compact
+-> moe_grouped_ffn -> moe_combine -- over one batch of the prefill layer
+(T=4096 tokens, E=128 experts all local, top-8 renormalised, hidden 2048,
+expert FFN 768, bf16, seeded synthetic inputs already resident in HBM).
+`value` is tokens/s of that layer.  One JSON line goes to stdout; progress
+goes to stderr.
+
+Besides the contract fields the line carries:
+  roofline      the grouped FFN call (GEMM1 + silu_and_mul kernel and GEMM2
+                kernel), its achieved bf16 MFMA TFLOP/s from HIP events on the
+                launch stream against the 2.5 PFLOP/s dense peak
+  cpu_baseline  the fp64 CPU oracle on a bounded token sample of the same
+                workload, on this host's cores
+  breakdown     per-call milliseconds of the step
+  secondary     gate throughput (65536 rows, E=128 and 160, bf16) in Mrows/s
+                and %-of-HBM with rotating buffers larger than the 256 MB
+                last-level cache; decode layer (M=2, top-6, 40 local
+                experts) per route pattern with achieved weight-stream GB/s
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-secondary", action="store_true")
+    p.add_argument("--quick", action="store_true", help="short secondary runs")
+    return p.parse_args()
+
+
+def bf16_dev(bits, dev):
+    import numpy as np
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def i32_dev(a, dev):
+    import numpy as np
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+
+def f32_dev(a, dev):
+    import numpy as np
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+
+# ---------------------------------------------------------------------------
+# main workload: the prefill layer
+
+
+def bench_prefill(args, dev):
+    import torch
+
+    import mixture_experts_routing_amd as moe
+    import synth
+
+    log("[bench] generating prefill layer inputs (T=4096, E=128, K=8, H=2048, F=768)")
+    c = synth.prefill_layer(0)
+    T, E, K, H, F = c.T, c.E_local, c.K, c.H, c.F
+    logits, x = bf16_dev(c.logits, dev), bf16_dev(c.x, dev)
+    w1, w2 = bf16_dev(c.w1, dev), bf16_dev(c.w2, dev)
+    N = T * K
+    # every output and workspace is allocated once, outside the timed region
+    tw = torch.empty((T, K), dtype=torch.float32, device=dev)
+    tid = torch.empty((T, K), dtype=torch.int32, device=dev)
+    tei = torch.empty((T, K), dtype=torch.int32, device=dev)
+    cmp_out = (torch.empty(E, dtype=torch.int32, device=dev), torch.empty(E + 1, dtype=torch.int32, device=dev),
+               torch.empty(N, dtype=torch.int32, device=dev), torch.empty(N, dtype=torch.int32, device=dev))
+    cws_n = moe.route_compact_workspace_bytes(T, K, E)
+    cws = torch.empty(max(cws_n, 16), dtype=torch.uint8, device=dev)
+    fws = torch.empty(moe.grouped_ffn_workspace_bytes(T, K, H, F, E, moe.MOE_BF16), dtype=torch.uint8, device=dev)
+    y = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        moe.moe_topk_softmax(logits, K, True, tw, tid, tei, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        counts, offsets, s2r, r2s = moe.moe_route_compact(tid, None, E, out=cmp_out, workspace=cws, stream=stream)
+        if ev:
+            ev[2].record(stream)
+        moe.moe_grouped_ffn(x, K, w1, w2, counts, offsets, r2s, y=y, workspace=fws, stream=stream)
+        if ev:
+            ev[3].record(stream)
+        moe.moe_combine(y, tw, s2r, out=out, stream=stream)
+        if ev:
+            ev[4].record(stream)
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = ["gate", "compact", "grouped_ffn", "combine"]
+    per = {n: 0.0 for n in names}
+    for ev in events:
+        for j, n in enumerate(names):
+            per[n] += ev[j].elapsed_time(ev[j + 1])
+    per = {n: v / args.steps for n, v in per.items()}
+    ms_per_step = wall * 1000.0 / args.steps
+    flops = 2.0 * N * (2 * F * H + H * F)  # all routes local: R = T*K
+    ffn_s = per["grouped_ffn"] / 1000.0
+    achieved = flops / ffn_s / 1e12
+    roofline = {
+        "bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic_for("grouped_ffn_prefill"),
+        "kernel": "moe_grouped_ffn (ffn1_stream_kernel + ffn2_stream_kernel)",
+        "algorithmic_flops_per_launch": flops, "avg_launch_ms": round(per["grouped_ffn"], 4),
+    }
+    log(f"[bench] prefill layer: {ms_per_step:.3f} ms/step, {T / (ms_per_step / 1e3):.0f} tokens/s; "
+        + ", ".join(f"{n} {v:.3f} ms" for n, v in per.items()))
+    return c, ms_per_step, per, roofline
+
+
+def traffic_for(name):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources (else None)."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+        if d.get("source_sha256") != kernel_source_hash():
+            return None
+        return d.get("bytes_per_launch")
+    except Exception:
+        return None
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mixture_experts_routing_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
+
+
+# ---------------------------------------------------------------------------
+# secondary: gate throughput with rotating buffers
+
+
+def bench_gate(dev, E, reps):
+    import torch
+
+    import mixture_experts_routing_amd as moe
+    import synth
+
+    T, K = 65536, 8
+    nbuf = 16  # 16 x T*E*2 bytes > 256 MB last-level cache
+    base = synth.gate_case(E, T=T, K=K, seed=0).logits
+    bufs = []
+    for i in range(nbuf):
+        lb = bf16_dev(base, dev).roll(i, dims=0).contiguous()
+        bufs.append((lb, torch.empty((T, K), dtype=torch.float32, device=dev),
+                     torch.empty((T, K), dtype=torch.int32, device=dev), torch.empty((T, K), dtype=torch.int32, device=dev)))
+    stream = torch.cuda.current_stream(dev)
+    for b in bufs:
+        moe.moe_topk_softmax(b[0], K, False, b[1], b[2], b[3], stream=stream)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for r in range(reps):
+        b = bufs[r % nbuf]
+        moe.moe_topk_softmax(b[0], K, False, b[1], b[2], b[3], stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / reps
+    nbytes = T * E * 2 + T * K * 12
+    gbs = nbytes / (ms / 1e3) / 1e9
+    return {"E": E, "T": T, "K": K, "ms": round(ms, 5), "mrows_per_s": round(T / (ms / 1e3) / 1e6, 1),
+            "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_call": nbytes}
+
+
+# ---------------------------------------------------------------------------
+# secondary: decode layer per route pattern
+
+
+def bench_decode(dev, reps):
+    import numpy as np
+    import torch
+
+    import mixture_experts_routing_amd as moe
+    import synth
+
+    log("[bench] decode: generating 40 bf16 experts (2.0 GB)")
+    w1h, w2h = synth.decode_weights(0)
+    w1, w2 = bf16_dev(w1h, dev), bf16_dev(w2h, dev)
+    del w1h, w2h
+    T, K, Eg, El, H, F = 2, 6, 256, 40, 4096, 2048
+    emap = synth.contiguous_expert_map(Eg, El)
+    emap_d = i32_dev(emap, dev)
+    inv = np.flatnonzero(emap >= 0)  # local -> global under the contiguous map
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    nvar = 8  # rotated copies of each pattern: consecutive calls touch different experts
+    for pat in synth.decode_patterns():
+        base = synth.decode_case(pat, "contiguous", seed=0, with_weights=False)
+        x = bf16_dev(base.x, dev)
+        tw = f32_dev(base.topk_weights, dev)
+        variants = []
+        for v in range(nvar):
+            rows = [[None if l is None else (l + 5 * v) % El for l in r] for r in synth.DECODE_PATTERNS[pat]]
+            ids = np.array([[int(inv[l]) if l is not None else int(base.topk_ids[t, k])
+                             for k, l in enumerate(r)] for t, r in enumerate(rows)], dtype=np.int32)
+            variants.append(i32_dev(ids, dev))
+        outs = (torch.empty(El, dtype=torch.int32, device=dev), torch.empty(El + 1, dtype=torch.int32, device=dev),
+                torch.empty(T * K, dtype=torch.int32, device=dev), torch.empty(T * K, dtype=torch.int32, device=dev))
+        fws = torch.empty(moe.grouped_ffn_workspace_bytes(T, K, H, F, El, moe.MOE_BF16), dtype=torch.uint8,
+                          device=dev)
+        y = torch.empty((T * K, H), dtype=torch.bfloat16, device=dev)
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+        def layer(ids, ev=None):
+            if ev:
+                ev[0].record(stream)
+            counts, offsets, s2r, r2s = moe.moe_route_compact(ids, emap_d, El, E_global=Eg, out=outs, stream=stream)
+            if ev:
+                ev[1].record(stream)
+            moe.moe_grouped_ffn(x, K, w1, w2, counts, offsets, r2s, y=y, workspace=fws, stream=stream)
+            if ev:
+                ev[2].record(stream)
+            moe.moe_combine(y, tw, s2r, out=out, stream=stream)
+            if ev:
+                ev[3].record(stream)
+
+        for v in range(nvar):
+            layer(variants[v])
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+        for r in range(reps):
+            layer(variants[r % nvar], evs[r])
+        torch.cuda.synchronize()
+        t_layer = sum(e[0].elapsed_time(e[3]) for e in evs) / reps
+        t_cmp = sum(e[0].elapsed_time(e[1]) for e in evs) / reps
+        t_ffn = sum(e[1].elapsed_time(e[2]) for e in evs) / reps
+        t_cmb = sum(e[2].elapsed_time(e[3]) for e in evs) / reps
+        n_exp = len({l for r in synth.DECODE_PATTERNS[pat] for l in r if l is not None})
+        wbytes = n_exp * (2 * F * H + H * F) * 2
+        d = {"layer_ms": round(t_layer, 4), "compact_ms": round(t_cmp, 4), "ffn_ms": round(t_ffn, 4),
+             "combine_ms": round(t_cmb, 4), "tokens_per_s": round(T / (t_layer / 1e3), 1),
+             "local_experts": n_exp, "weight_bytes": wbytes}
+        if wbytes:
+            gbs = wbytes / (t_ffn / 1e3) / 1e9
+            d.update({"ffn_weight_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+        res[pat] = d
+        log(f"[bench] decode {pat}: " + json.dumps(d))
+    nonempty = [p for p in res if res[p]["local_experts"] > 0]
+    worst = min(nonempty, key=lambda p: res[p]["hbm_frac"])
+    return {"patterns": res, "min_hbm_frac_pattern": worst, "min_hbm_frac": res[worst]["hbm_frac"],
+            "min_tokens_per_s": min(res[p]["tokens_per_s"] for p in res)}
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the prefill workload
+
+
+def cpu_baseline(c, n_tokens):
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    import synth
+
+    sub = synth.MoECase(**{**c.__dict__})
+    sub.T = n_tokens
+    sub.logits = c.logits[:n_tokens]
+    sub.x = c.x[:n_tokens]
+    t0 = time.perf_counter()
+    oracle.moe_layer(sub)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": round(n_tokens / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n_tokens} of the {c.T} prefill tokens (gate, compaction, fp64 FFN of all "
+                      f"{n_tokens * c.K} routes over the 128 experts, combine); {dt:.1f} s wall",
+            "host_cores_available": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 (the path would shard by "
+                                   "experts across GPUs, which is not built)"}))
+        sys.exit(2)
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    c, ms, per, roofline = bench_prefill(args, dev)
+    secondary = {}
+    if not args.no_secondary:
+        reps = 50 if args.quick else 400
+        secondary["gate"] = [bench_gate(dev, E, reps) for E in (128, 160)]
+        for g in secondary["gate"]:
+            log(f"[bench] gate E={g['E']}: {g['ms'] * 1e3:.2f} us, {g['mrows_per_s']} Mrows/s, "
+                f"{g['gbs']} GB/s ({100 * g['hbm_frac']:.1f}% of HBM)")
+        secondary["decode"] = bench_decode(dev, 16 if args.quick else 80)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline")
+        cpu = cpu_baseline(c, 1024 if args.quick else c.T)
+        log(f"[bench] cpu: {cpu}")
+    line = {
+        "metric": "MoE-layer tokens/s + gate Mrows/s; % of HBM BW / MFMA peak, 1 MI355X",
+        "value": round(c.T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "prefill_moe_layer", "tokens": c.T, "experts": c.E_local, "top_k": c.K,
+                   "renormalize": True, "hidden": c.H, "expert_ffn": c.F, "weights": "bf16",
+                   "parallelism": "single-gpu"},
+        "roofline": roofline, "cpu_baseline": cpu, "breakdown_ms": {k: round(v, 4) for k, v in per.items()},
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

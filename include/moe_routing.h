@@ -1,0 +1,170 @@
+/*
+ * moe_routing.h -- C ABI of the MI355X (gfx950) MoE routing + expert-FFN hot path.
+ *
+ * The library runs one MoE layer's data path on one GPU, in the order of the
+ * FusedMoE pipeline "gate -> topk -> expand -> gemm1 -> act -> gemm2 -> combine"
+ * (page "Upstream Reference: Deep-Spark xllm + vllm", section "File Index"):
+ *
+ *   moe_topk_softmax   fused softmax + top-k over router logits
+ *   moe_route_compact  per-local-expert row counts, row prefix and the
+ *                      slot <-> row permutation of the expert-grouped layout
+ *   moe_grouped_ffn    expand (gather) -> GEMM1 -> silu_and_mul -> GEMM2 per
+ *                      local expert, weights read once per expert tile
+ *   moe_combine        top-k weighted slot-order gather back to token order
+ *
+ * Conventions shared by every entry point
+ *   - Every array argument is caller-owned DEVICE memory (hipMalloc'd or a
+ *     torch tensor's data_ptr()), contiguous and row-major, unless stated.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
+ *     enqueued on it; no call synchronises, allocates, frees, or reads device
+ *     data on the host, so a sequence of calls can be captured in a graph.
+ *   - A slot is s = t*K + k for token t and rank k.  N = T*K slots.
+ *   - Return value: MOE_OK, or an error code.  Argument checks run on the
+ *     host before anything is launched; on an error nothing is enqueued and
+ *     the outputs are untouched.  MOE_ERR_HIP means a launch failed
+ *     (moe_last_hip_error() gives the hipError_t).  T == 0 is a valid no-op.
+ *   - Device-side preconditions (not checked on the host): logits are
+ *     finite; topk_ids lie in [0, E_global); expert_map values lie in
+ *     [-1, E_local).  Out-of-range ids or map values are treated as remote
+ *     routes (memory-safe, deterministic), never read out of bounds.
+ *   - Outputs are deterministic: identical inputs give bit-identical outputs.
+ */
+#ifndef MOE_ROUTING_H
+#define MOE_ROUTING_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null pointer, negative or inconsistent size */
+  MOE_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels implement */
+  MOE_ERR_HIP = 3,         /* a HIP launch or device query failed */
+  MOE_ERR_WORKSPACE = 4    /* workspace missing or smaller than required */
+} moe_status;
+
+typedef enum moe_dtype {
+  MOE_F32 = 0,   /* IEEE binary32 */
+  MOE_BF16 = 1,  /* bfloat16, round-to-nearest-even on every store */
+  MOE_MXFP4 = 2  /* OCP MX FP4 (E2M1) codes, 2 per byte, element 2i in the low
+                    nibble, plus one E8M0 scale byte (2^(e-127)) per 32
+                    consecutive elements of the reduction dimension */
+} moe_dtype;
+
+/*
+ * moe_topk_softmax -- fused softmax + top-k gate.
+ * Source: page "Upstream Reference: Deep-Spark xllm + vllm", section "Call
+ * Chain: MoE topk_softmax on BI-V100" (a fused topk_softmax op returning the
+ * routing weights, the expert ids and a token-expert index map).
+ *
+ *   logits               [T, E], MOE_F32 or MOE_BF16 (logits_dtype)
+ *   topk_weights (out)   [T, K] float: softmax(logits[t])[topk_ids[t,k]];
+ *                        with renormalize != 0 divided by the sum over the
+ *                        row's K chosen experts (remote experts included)
+ *   topk_ids (out)       [T, K] int32: the K largest logits of the row, best
+ *                        first; equal logits rank the lower expert index first
+ *   token_expert_indices [T, K] int32 (out, may be NULL): k*T + t, the slot's
+ *                        source row in a k-major expanded layout
+ * Limits: 1 <= E <= 1280, 1 <= K <= min(E, 32).  Weights are computed in
+ * fp32 (max relative error vs exact softmax ~5e-7).
+ */
+int moe_topk_softmax(const void* logits, int logits_dtype, int64_t T, int32_t E, int32_t K,
+                     int32_t renormalize, float* topk_weights, int32_t* topk_ids,
+                     int32_t* token_expert_indices, void* stream);
+
+/*
+ * moe_route_compact -- route compaction for one expert-parallel rank.
+ * Source: b70-optimization-lab note "MTP1 M2 compact scheduler closure"
+ * (2026-07-16), design paragraph: derive each local expert's row count and
+ * remapped-row prefix on device from topk_ids plus expert_map, keeping the
+ * expert-grouped activation layout; duplicate routes and an all-remote rank
+ * are valid inputs.
+ *
+ *   topk_ids     [T*K] int32 global expert ids
+ *   expert_map   [E_global] int32 global -> local id, -1 = remote; NULL means
+ *                identity (then E_local must equal E_global)
+ *   counts (out)      [E_local] rows routed to each local expert
+ *   offsets (out)     [E_local + 1] exclusive prefix of counts; offsets[E_local] = R
+ *   slot_to_row (out) [T*K] row of each slot in the grouped layout, -1 if remote
+ *   row_to_slot (out) [T*K] inverse: slot of row r for r < R, -1 for r >= R
+ * Rows of one expert are in slot order (a stable counting sort by local id);
+ * every slot gets its own row, duplicates included.
+ * workspace: device scratch of moe_route_compact_workspace_bytes(T, K, E_local)
+ * bytes (may be 0 bytes/NULL when that function returns 0).
+ * Limits: 1 <= E_local <= 768, E_local <= E_global, T*K < 2^31.
+ */
+int moe_route_compact(const int32_t* topk_ids, int64_t T, int32_t K, const int32_t* expert_map,
+                      int32_t E_global, int32_t E_local, int32_t* counts, int32_t* offsets,
+                      int32_t* slot_to_row, int32_t* row_to_slot, void* workspace,
+                      size_t workspace_bytes, void* stream);
+size_t moe_route_compact_workspace_bytes(int64_t T, int32_t K, int32_t E_local);
+
+/*
+ * moe_grouped_ffn -- expert-grouped SwiGLU FFN over the compacted rows.
+ * Sources: page "Upstream Reference: Deep-Spark xllm + vllm", section "File
+ * Index" (expand -> gemm1 -> act (silu_and_mul) -> gemm2); b70 lab note
+ * "MTP1 M2 compact scheduler closure", design paragraph (expert-grouped
+ * layout, one weight pass shared by every row routed to the same expert).
+ *
+ * For every row r < R of the grouped layout, with e the local expert owning
+ * r (offsets[e] <= r < offsets[e+1]) and t = row_to_slot[r] / K:
+ *   h      = W1[e] x[t]                      (fp32 accumulation)
+ *   act    = silu(h[0:F]) * h[F:2F]          silu(g) = g / (1 + exp(-g))
+ *   y[r]   = W2[e] act                       (fp32 accumulation)
+ *   x        [T, H]            MOE_F32 or MOE_BF16 (x_dtype)
+ *   w1       [E_local, 2F, H]  gate rows [0,F), up rows [F,2F); MOE_F32/MOE_BF16,
+ *                              or MXFP4 codes [E_local, 2F, H/2] with
+ *                              w1_scale [E_local, 2F, H/32]
+ *   w2       [E_local, H, F]   or MXFP4 codes [E_local, H, F/2] with
+ *                              w2_scale [E_local, H, F/32]
+ *   counts, offsets, row_to_slot: as produced by moe_route_compact
+ *   y (out)  [T*K, H] (y_dtype MOE_F32 or MOE_BF16); rows >= R are not written
+ * Supported (x, w) pairs: (F32, F32), (BF16, BF16), (BF16, MXFP4).
+ * The intermediate act is kept in the workspace in bf16 for bf16/MXFP4
+ * weights and in fp32 for fp32 weights.
+ * workspace: moe_grouped_ffn_workspace_bytes(...) bytes of device scratch.
+ * Limits: H and F multiples of 32 for bf16/MXFP4 (of 1 for f32); H, F >= 1.
+ */
+int moe_grouped_ffn(const void* x, int x_dtype, int64_t T, int32_t K, int32_t H, int32_t F,
+                    int32_t E_local, const void* w1, const uint8_t* w1_scale, const void* w2,
+                    const uint8_t* w2_scale, int w_dtype, const int32_t* counts,
+                    const int32_t* offsets, const int32_t* row_to_slot, void* y, int y_dtype,
+                    void* workspace, size_t workspace_bytes, void* stream);
+size_t moe_grouped_ffn_workspace_bytes(int64_t T, int32_t K, int32_t H, int32_t F, int32_t E_local,
+                                       int w_dtype);
+
+/*
+ * moe_combine -- top-k weighted combine (direct slot-order gather).
+ * Source: b70 lab note "MTP1 M2 compact scheduler closure", correctness
+ * paragraph (direct slot-order gather as the reference combine) and its
+ * next-screen paragraph (the final permuted gather boundary).
+ *
+ *   out[t, :] = sum over k = 0..K-1 (ascending) with slot_to_row[t*K+k] >= 0
+ *               of topk_weights[t, k] * y[slot_to_row[t*K+k], :]
+ * fp32 accumulation, one rounding to out_dtype.  Remote slots contribute
+ * nothing: this is the partial sum of one expert-parallel rank, and a token
+ * with only remote routes gets exact zeros.
+ *   y [R, H] (y_dtype), topk_weights [T, K] float, slot_to_row [T*K] int32,
+ *   out (out) [T, H] (out_dtype MOE_F32 or MOE_BF16)
+ */
+int moe_combine(const void* y, int y_dtype, const float* topk_weights, const int32_t* slot_to_row,
+                int64_t T, int32_t K, int32_t H, void* out, int out_dtype, void* stream);
+
+/* Human-readable name of a moe_status value (static string). */
+const char* moe_status_string(int status);
+
+/* The hipError_t of the most recent MOE_ERR_HIP on the calling thread (0 if none). */
+int moe_last_hip_error(void);
+
+/* Library version string (static). */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ROUTING_H */

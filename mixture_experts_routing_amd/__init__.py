@@ -1,0 +1,185 @@
+"""MI355X-native MoE routing + expert-FFN hot path.
+
+Thin Python binding over the C ABI of libmoe_routing.so (include/moe_routing.h).
+The functions below only marshal torch tensors (device memory) and the
+current HIP stream into the C calls; every step of the path runs in the HIP
+kernels of the library.  Importing this package fails if the library has not
+been built: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import MOE_BF16, MOE_F32, MOE_MXFP4
+
+_LIB = _lib.load()
+
+__all__ = [
+    "moe_topk_softmax", "moe_route_compact", "moe_grouped_ffn", "moe_combine", "moe_layer",
+    "MOE_F32", "MOE_BF16", "MOE_MXFP4", "MoeError", "library_path",
+]
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        msg = _lib.status_string(code)
+        if code == _lib.MOE_ERR_HIP:
+            msg += f" (hipError {_LIB.moe_last_hip_error()})"
+        raise MoeError(f"{what}: {msg}")
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must live in GPU memory")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+        dev = t.device if dev is None else dev
+        if t.device != dev:
+            raise ValueError("tensors on different devices")
+    return dev
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+def moe_topk_softmax(logits: torch.Tensor, K: int, renormalize: bool = False,
+                     topk_weights: Optional[torch.Tensor] = None, topk_ids: Optional[torch.Tensor] = None,
+                     token_expert_indices: Optional[torch.Tensor] = None, with_indices: bool = True,
+                     stream=None) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
+    """logits [T, E] (f32 or bf16) -> (weights f32 [T,K], ids i32 [T,K], token_expert_indices i32 [T,K])."""
+    dev = _dev(logits)
+    T, E = logits.shape
+    if topk_weights is None:
+        topk_weights = torch.empty((T, K), dtype=torch.float32, device=dev)
+    if topk_ids is None:
+        topk_ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+    if token_expert_indices is None and with_indices:
+        token_expert_indices = torch.empty((T, K), dtype=torch.int32, device=dev)
+    _dev(topk_weights, topk_ids, token_expert_indices)
+    _check(_LIB.moe_topk_softmax(_ptr(logits), _dt(logits), T, E, K, int(bool(renormalize)), _ptr(topk_weights),
+                                 _ptr(topk_ids), _ptr(token_expert_indices), _stream(stream, dev)),
+           "moe_topk_softmax")
+    return topk_weights, topk_ids, token_expert_indices
+
+
+def route_compact_workspace_bytes(T: int, K: int, E_local: int) -> int:
+    return int(_LIB.moe_route_compact_workspace_bytes(T, K, E_local))
+
+
+def moe_route_compact(topk_ids: torch.Tensor, expert_map: Optional[torch.Tensor], E_local: int,
+                      E_global: Optional[int] = None, out=None, workspace: Optional[torch.Tensor] = None,
+                      stream=None):
+    """topk_ids [T, K] int32 (global ids), expert_map [E_global] int32 or None
+    -> (counts [E_local], offsets [E_local+1], slot_to_row [T*K], row_to_slot [T*K]), all int32."""
+    dev = _dev(topk_ids, expert_map)
+    T, K = topk_ids.shape
+    if E_global is None:
+        E_global = expert_map.numel() if expert_map is not None else E_local
+    if out is None:
+        counts = torch.empty(E_local, dtype=torch.int32, device=dev)
+        offsets = torch.empty(E_local + 1, dtype=torch.int32, device=dev)
+        s2r = torch.empty(T * K, dtype=torch.int32, device=dev)
+        r2s = torch.empty(T * K, dtype=torch.int32, device=dev)
+    else:
+        counts, offsets, s2r, r2s = out
+    need = route_compact_workspace_bytes(T, K, E_local)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_LIB.moe_route_compact(_ptr(topk_ids), T, K, _ptr(expert_map), E_global, E_local, _ptr(counts),
+                                  _ptr(offsets), _ptr(s2r), _ptr(r2s), _ptr(workspace), ws_bytes,
+                                  _stream(stream, dev)), "moe_route_compact")
+    return counts, offsets, s2r, r2s
+
+
+def grouped_ffn_workspace_bytes(T: int, K: int, H: int, F: int, E_local: int, w_dtype: int) -> int:
+    return int(_LIB.moe_grouped_ffn_workspace_bytes(T, K, H, F, E_local, w_dtype))
+
+
+def moe_grouped_ffn(x: torch.Tensor, K: int, w1: torch.Tensor, w2: torch.Tensor, counts: torch.Tensor,
+                    offsets: torch.Tensor, row_to_slot: torch.Tensor, w1_scale: Optional[torch.Tensor] = None,
+                    w2_scale: Optional[torch.Tensor] = None, y_dtype: Optional[torch.dtype] = None,
+                    y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None):
+    """x [T, H]; w1 [E_local, 2F, H] and w2 [E_local, H, F] (f32 / bf16), or
+    uint8 MXFP4 codes [E_local, 2F, H/2], [E_local, H, F/2] with e8m0 scales.
+    Returns y [T*K, H] in the expert-grouped row order (rows >= R unwritten)."""
+    dev = _dev(x, w1, w2, counts, offsets, row_to_slot, w1_scale, w2_scale)
+    T, H = x.shape
+    E_local = w1.shape[0]
+    if w1.dtype == torch.uint8:
+        w_dt = MOE_MXFP4
+        F = w2.shape[2] * 2
+    else:
+        w_dt = _dt(w1)
+        F = w2.shape[2]
+    if y is None:
+        y = torch.empty((T * K, H), dtype=y_dtype or x.dtype, device=dev)
+    need = grouped_ffn_workspace_bytes(T, K, H, F, E_local, w_dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _check(_LIB.moe_grouped_ffn(_ptr(x), _dt(x), T, K, H, F, E_local, _ptr(w1), _ptr(w1_scale), _ptr(w2),
+                                _ptr(w2_scale), w_dt, _ptr(counts), _ptr(offsets), _ptr(row_to_slot), _ptr(y),
+                                _dt(y), _ptr(workspace), workspace.numel(), _stream(stream, dev)),
+           "moe_grouped_ffn")
+    return y
+
+
+def moe_combine(y: torch.Tensor, topk_weights: torch.Tensor, slot_to_row: torch.Tensor,
+                out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None, stream=None):
+    """y [R', H] grouped rows, topk_weights [T, K] f32, slot_to_row [T*K] -> out [T, H]."""
+    dev = _dev(y, topk_weights, slot_to_row)
+    T, K = topk_weights.shape
+    H = y.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype or y.dtype, device=dev)
+    _check(_LIB.moe_combine(_ptr(y), _dt(y), _ptr(topk_weights), _ptr(slot_to_row), T, K, H, _ptr(out), _dt(out),
+                            _stream(stream, dev)), "moe_combine")
+    return out
+
+
+def moe_layer(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, K: int, logits: Optional[torch.Tensor] = None,
+              renormalize: bool = False, topk_ids: Optional[torch.Tensor] = None,
+              topk_weights: Optional[torch.Tensor] = None, expert_map: Optional[torch.Tensor] = None,
+              E_global: Optional[int] = None, w1_scale=None, w2_scale=None, out_dtype=None, y_dtype=None,
+              stream=None) -> dict:
+    """The whole path: gate (if logits are given) -> compaction -> grouped FFN -> combine."""
+    tei = None
+    if logits is not None:
+        topk_weights, topk_ids, tei = moe_topk_softmax(logits, K, renormalize, stream=stream)
+    E_local = w1.shape[0]
+    counts, offsets, s2r, r2s = moe_route_compact(topk_ids, expert_map, E_local, E_global=E_global, stream=stream)
+    y = moe_grouped_ffn(x, K, w1, w2, counts, offsets, r2s, w1_scale, w2_scale, y_dtype=y_dtype or x.dtype,
+                        stream=stream)
+    out = moe_combine(y, topk_weights, s2r, out_dtype=out_dtype or x.dtype, stream=stream)
+    return dict(topk_weights=topk_weights, topk_ids=topk_ids, token_expert_indices=tei, counts=counts,
+                offsets=offsets, slot_to_row=s2r, row_to_slot=r2s, y=y, out=out)

@@ -1,0 +1,119 @@
+// Top-k weighted combine: the direct slot-order gather of the b70 lab note
+// "MTP1 M2 compact scheduler closure" (correctness paragraph), i.e. the
+// FusedMoE "combine" step.
+//
+//   out[t, :] = sum_{k ascending, slot_to_row[t*K+k] >= 0} w[t,k] * y[row, :]
+//
+// One block per token; each thread owns 8 consecutive hidden elements (one
+// 16-byte load of a bf16 row) and walks the token's K slots in order, so the
+// fp32 accumulation order is fixed.  Slot rows and weights are wave-uniform
+// and come through the scalar cache.  HBM-bound: it reads R*H elements of y
+// and writes T*H outputs.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename YT>
+__device__ __forceinline__ void load8(const YT* p, float (&v)[8]) {
+  if constexpr (sizeof(YT) == 2) {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(p);
+    v[0] = bf16_bits_to_f32(q.x & 0xFFFFu); v[1] = bf16_bits_to_f32(q.x >> 16);
+    v[2] = bf16_bits_to_f32(q.y & 0xFFFFu); v[3] = bf16_bits_to_f32(q.y >> 16);
+    v[4] = bf16_bits_to_f32(q.z & 0xFFFFu); v[5] = bf16_bits_to_f32(q.z >> 16);
+    v[6] = bf16_bits_to_f32(q.w & 0xFFFFu); v[7] = bf16_bits_to_f32(q.w >> 16);
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+template <typename OT>
+__device__ __forceinline__ void store8(OT* p, const float (&v)[8]) {
+  if constexpr (sizeof(OT) == 2) {
+    u32x4 q;
+    q.x = pack_bf16x2(v[0], v[1]); q.y = pack_bf16x2(v[2], v[3]);
+    q.z = pack_bf16x2(v[4], v[5]); q.w = pack_bf16x2(v[6], v[7]);
+    *reinterpret_cast<u32x4*>(p) = q;
+  } else {
+    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+  }
+}
+
+template <typename YT>
+__device__ __forceinline__ float load1(const YT* p) {
+  if constexpr (sizeof(YT) == 2) return bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(p));
+  else return *p;
+}
+template <typename OT>
+__device__ __forceinline__ void store1(OT* p, float v) {
+  if constexpr (sizeof(OT) == 2) *reinterpret_cast<uint16_t*>(p) = f32_to_bf16_bits(v);
+  else *p = v;
+}
+
+// YT/OT: uint16_t (bf16 bits) or float
+template <typename YT, typename OT, bool VEC>
+__global__ __launch_bounds__(kThreads) void combine_kernel(const YT* __restrict__ y, const float* __restrict__ w,
+                                                          const int32_t* __restrict__ s2r, int64_t T, int K,
+                                                          int H, OT* __restrict__ out) {
+  const int64_t t = blockIdx.x;
+  const int32_t* rows = s2r + t * K;
+  const float* wt = w + t * K;
+  if constexpr (VEC) {
+    for (int c = threadIdx.x * 8; c < H; c += kThreads * 8) {
+      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int k = 0; k < K; ++k) {
+        const int r = rows[k];
+        if (r < 0) continue;
+        const float wk = wt[k];
+        float v[8];
+        load8(y + (int64_t)r * H + c, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wk, v[i], acc[i]);
+      }
+      store8(out + t * H + c, acc);
+    }
+  } else {
+    for (int c = threadIdx.x; c < H; c += kThreads) {
+      float acc = 0.0f;
+      for (int k = 0; k < K; ++k) {
+        const int r = rows[k];
+        if (r < 0) continue;
+        acc = fmaf(wt[k], load1(y + (int64_t)r * H + c), acc);
+      }
+      store1(out + t * H + c, acc);
+    }
+  }
+}
+
+template <typename YT, typename OT>
+hipError_t launch_typed(const void* y, const float* w, const int32_t* s2r, int64_t T, int K, int H, void* out,
+                        hipStream_t stream) {
+  const YT* yp = static_cast<const YT*>(y);
+  OT* op = static_cast<OT*>(out);
+  const bool vec = (H % 8 == 0) && ((uintptr_t)y % 16 == 0) && ((uintptr_t)out % 16 == 0);
+  if (vec)
+    hipLaunchKernelGGL((combine_kernel<YT, OT, true>), dim3((unsigned)T), dim3(kThreads), 0, stream, yp, w, s2r,
+                       T, K, H, op);
+  else
+    hipLaunchKernelGGL((combine_kernel<YT, OT, false>), dim3((unsigned)T), dim3(kThreads), 0, stream, yp, w, s2r,
+                       T, K, H, op);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_combine(const void* y, int y_dtype, const float* w, const int32_t* s2r, int64_t T, int K, int H,
+                          void* out, int out_dtype, hipStream_t stream) {
+  if (y_dtype == MOE_BF16 && out_dtype == MOE_BF16) return launch_typed<uint16_t, uint16_t>(y, w, s2r, T, K, H, out, stream);
+  if (y_dtype == MOE_BF16 && out_dtype == MOE_F32) return launch_typed<uint16_t, float>(y, w, s2r, T, K, H, out, stream);
+  if (y_dtype == MOE_F32 && out_dtype == MOE_BF16) return launch_typed<float, uint16_t>(y, w, s2r, T, K, H, out, stream);
+  return launch_typed<float, float>(y, w, s2r, T, K, H, out, stream);
+}
+
+}  // namespace moe

@@ -1,0 +1,120 @@
+// C ABI entry points: host-side argument checks, then the launchers.
+// Every check runs before anything is enqueued, so an error leaves the
+// outputs untouched and the stream unchanged.
+#include "moe_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_hip_error = (int)e;
+  return MOE_ERR_HIP;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_version(void) { return "moe_routing 0.1 (gfx950)"; }
+
+const char* moe_status_string(int s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+int moe_last_hip_error(void) { return g_last_hip_error; }
+
+int moe_topk_softmax(const void* logits, int logits_dtype, int64_t T, int32_t E, int32_t K, int32_t renormalize,
+                     float* topk_weights, int32_t* topk_ids, int32_t* token_expert_indices, void* stream) {
+  if (T < 0 || E < 1 || K < 1 || K > E) return MOE_ERR_INVALID_ARG;
+  if (logits_dtype != MOE_F32 && logits_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (E > 1280 || K > 32) return MOE_ERR_UNSUPPORTED;
+  if (T > ((int64_t)1 << 31) / K) return MOE_ERR_UNSUPPORTED;  // k*T + t must fit int32
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_weights || !topk_ids) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_topk_softmax(logits, logits_dtype, T, E, K, renormalize != 0, topk_weights, topk_ids,
+                                             token_expert_indices, static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_route_compact_workspace_bytes(int64_t T, int32_t K, int32_t E_local) {
+  if (T <= 0 || K <= 0 || E_local <= 0) return 0;
+  return moe::route_compact_workspace_bytes(T * K, E_local);
+}
+
+int moe_route_compact(const int32_t* topk_ids, int64_t T, int32_t K, const int32_t* expert_map, int32_t E_global,
+                      int32_t E_local, int32_t* counts, int32_t* offsets, int32_t* slot_to_row,
+                      int32_t* row_to_slot, void* workspace, size_t workspace_bytes, void* stream) {
+  if (T < 0 || K < 1 || E_local < 1 || E_global < 1 || E_local > E_global) return MOE_ERR_INVALID_ARG;
+  if (!expert_map && E_local != E_global) return MOE_ERR_INVALID_ARG;
+  if (E_local > 768) return MOE_ERR_UNSUPPORTED;
+  if (T * (int64_t)K >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
+  const int64_t N = T * K;
+  if (N > 0 && (!topk_ids || !slot_to_row || !row_to_slot)) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe::route_compact_workspace_bytes(N, E_local);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MOE_ERR_WORKSPACE;
+  // T == 0 still defines counts = 0 and offsets = 0: run the (cheap) kernel
+  return hip_status(moe::launch_route_compact(topk_ids, N, expert_map, E_global, E_local, counts, offsets,
+                                              slot_to_row, row_to_slot, workspace, static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_grouped_ffn_workspace_bytes(int64_t T, int32_t K, int32_t H, int32_t F, int32_t E_local, int w_dtype) {
+  (void)H;
+  (void)E_local;
+  if (T <= 0 || K <= 0 || F <= 0) return 0;
+  return moe::grouped_ffn_workspace_bytes(T * K, F, w_dtype);
+}
+
+int moe_grouped_ffn(const void* x, int x_dtype, int64_t T, int32_t K, int32_t H, int32_t F, int32_t E_local,
+                    const void* w1, const uint8_t* w1_scale, const void* w2, const uint8_t* w2_scale, int w_dtype,
+                    const int32_t* counts, const int32_t* offsets, const int32_t* row_to_slot, void* y, int y_dtype,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (T < 0 || K < 1 || H < 1 || F < 1 || E_local < 1) return MOE_ERR_INVALID_ARG;
+  if (y_dtype != MOE_F32 && y_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  const bool f32_pair = (x_dtype == MOE_F32 && w_dtype == MOE_F32);
+  const bool bf16_pair = (x_dtype == MOE_BF16 && w_dtype == MOE_BF16);
+  const bool mx_pair = (x_dtype == MOE_BF16 && w_dtype == MOE_MXFP4);
+  if (!f32_pair && !bf16_pair && !mx_pair) return MOE_ERR_UNSUPPORTED;
+  if (!f32_pair && (H % 32 != 0 || F % 32 != 0)) return MOE_ERR_UNSUPPORTED;
+  if (T * (int64_t)K >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  if (f32_pair && T * (int64_t)K * (int64_t)(H > F ? H : F) >= ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !w1 || !w2 || !counts || !offsets || !row_to_slot || !y) return MOE_ERR_INVALID_ARG;
+  if (mx_pair && (!w1_scale || !w2_scale)) return MOE_ERR_INVALID_ARG;
+  if (!f32_pair) {
+    // bf16 rows are read as 16-byte vectors
+    if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16)) return MOE_ERR_INVALID_ARG;
+  }
+  const size_t need = moe::grouped_ffn_workspace_bytes(T * K, F, w_dtype);
+  if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_grouped_ffn(x, x_dtype, T, K, H, F, E_local, w1, w1_scale, w2, w2_scale, w_dtype,
+                                            counts, offsets, row_to_slot, y, y_dtype, workspace,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int moe_combine(const void* y, int y_dtype, const float* topk_weights, const int32_t* slot_to_row, int64_t T,
+                int32_t K, int32_t H, void* out, int out_dtype, void* stream) {
+  if (T < 0 || K < 1 || H < 1) return MOE_ERR_INVALID_ARG;
+  if ((y_dtype != MOE_F32 && y_dtype != MOE_BF16) || (out_dtype != MOE_F32 && out_dtype != MOE_BF16))
+    return MOE_ERR_UNSUPPORTED;
+  if (T >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!topk_weights || !slot_to_row || !out) return MOE_ERR_INVALID_ARG;
+  // y may be NULL only if nothing is local; that cannot be known on the host
+  if (!y) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_combine(y, y_dtype, topk_weights, slot_to_row, T, K, H, out, out_dtype,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

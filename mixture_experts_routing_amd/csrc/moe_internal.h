@@ -1,0 +1,137 @@
+// Internal declarations shared by the library's translation units: device
+// helpers (bf16 conversion, wave-level DPP reductions) and the host-side
+// launchers that the C ABI layer calls after validating arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe_routing.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// scalar conversions
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// float -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// DPP lane exchanges inside a wave.  Every pattern used here reads a lane of
+// the same 16-lane row that always exists, so bound_ctrl never zero-fills; it
+// is set so that the compiler folds the move into the consuming ALU op.
+// Callers keep EXEC full around these helpers.
+
+enum : int {
+  DPP_QUAD_XOR1 = 0xB1,    // quad_perm [1,0,3,2]
+  DPP_QUAD_XOR2 = 0x4E,    // quad_perm [2,3,0,1]
+  DPP_ROW_HALF_MIRROR = 0x141,  // lane i <- lane 7-i within each 8
+  DPP_ROW_MIRROR = 0x140,       // lane i <- lane 15-i within each 16
+};
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int x) {
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, true);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Value of lane (lane ^ m) for m in {16, 32}: crosses 16-lane rows, so it
+// goes through ds_swizzle/bpermute rather than DPP.
+__device__ __forceinline__ int xor_lane_i32(int x, int m) { return __shfl_xor(x, m, 64); }
+__device__ __forceinline__ float xor_lane_f32(float x, int m) { return __shfl_xor(x, m, 64); }
+
+// Max over each aligned group of G lanes (G a power of two <= 64); every lane
+// of the group receives the result.
+template <int G>
+__device__ __forceinline__ int group_max_i32(int x) {
+  if constexpr (G >= 2) x = max(x, dpp_i32<DPP_QUAD_XOR1>(x));
+  if constexpr (G >= 4) x = max(x, dpp_i32<DPP_QUAD_XOR2>(x));
+  if constexpr (G >= 8) x = max(x, dpp_i32<DPP_ROW_HALF_MIRROR>(x));
+  if constexpr (G >= 16) x = max(x, dpp_i32<DPP_ROW_MIRROR>(x));
+  if constexpr (G >= 32) x = max(x, xor_lane_i32(x, 16));
+  if constexpr (G >= 64) x = max(x, xor_lane_i32(x, 32));
+  return x;
+}
+
+// 64-bit keys: exchange both halves, compare as signed 64-bit.
+template <int CTRL>
+__device__ __forceinline__ int64_t dpp_i64(int64_t x) {
+  int lo = dpp_i32<CTRL>((int)(uint32_t)x);
+  int hi = dpp_i32<CTRL>((int)(x >> 32));
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+__device__ __forceinline__ int64_t xor_lane_i64(int64_t x, int m) {
+  int lo = __shfl_xor((int)(uint32_t)x, m, 64);
+  int hi = __shfl_xor((int)(x >> 32), m, 64);
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+template <int G>
+__device__ __forceinline__ int64_t group_max_i64(int64_t x) {
+  if constexpr (G >= 2) { int64_t y = dpp_i64<DPP_QUAD_XOR1>(x); x = x > y ? x : y; }
+  if constexpr (G >= 4) { int64_t y = dpp_i64<DPP_QUAD_XOR2>(x); x = x > y ? x : y; }
+  if constexpr (G >= 8) { int64_t y = dpp_i64<DPP_ROW_HALF_MIRROR>(x); x = x > y ? x : y; }
+  if constexpr (G >= 16) { int64_t y = dpp_i64<DPP_ROW_MIRROR>(x); x = x > y ? x : y; }
+  if constexpr (G >= 32) { int64_t y = xor_lane_i64(x, 16); x = x > y ? x : y; }
+  if constexpr (G >= 64) { int64_t y = xor_lane_i64(x, 32); x = x > y ? x : y; }
+  return x;
+}
+
+// Sum over each aligned group of G lanes.  Each step adds a lane's partial to
+// its partner's (a + b == b + a), so every lane of the group ends with the
+// bit-identical sum, in a fixed order.
+template <int G>
+__device__ __forceinline__ float group_sum_f32(float x) {
+  if constexpr (G >= 2) x += dpp_f32<DPP_QUAD_XOR1>(x);
+  if constexpr (G >= 4) x += dpp_f32<DPP_QUAD_XOR2>(x);
+  if constexpr (G >= 8) x += dpp_f32<DPP_ROW_HALF_MIRROR>(x);
+  if constexpr (G >= 16) x += dpp_f32<DPP_ROW_MIRROR>(x);
+  if constexpr (G >= 32) x += xor_lane_f32(x, 16);
+  if constexpr (G >= 64) x += xor_lane_f32(x, 32);
+  return x;
+}
+
+// ---------------------------------------------------------------------------
+// host-side launchers (one per kernel family), called after validation
+
+hipError_t launch_topk_softmax(const void* logits, int logits_dtype, int64_t T, int E, int K,
+                               int renormalize, float* w, int32_t* ids, int32_t* tei,
+                               hipStream_t stream);
+
+size_t route_compact_workspace_bytes(int64_t N, int E_local);
+hipError_t launch_route_compact(const int32_t* topk_ids, int64_t N, const int32_t* expert_map,
+                                int E_global, int E_local, int32_t* counts, int32_t* offsets,
+                                int32_t* slot_to_row, int32_t* row_to_slot, void* workspace,
+                                hipStream_t stream);
+
+size_t grouped_ffn_workspace_bytes(int64_t N, int F, int w_dtype);
+hipError_t launch_grouped_ffn(const void* x, int x_dtype, int64_t T, int K, int H, int F,
+                              int E_local, const void* w1, const uint8_t* w1s, const void* w2,
+                              const uint8_t* w2s, int w_dtype, const int32_t* counts,
+                              const int32_t* offsets, const int32_t* row_to_slot, void* y,
+                              int y_dtype, void* workspace, hipStream_t stream);
+
+hipError_t launch_combine(const void* y, int y_dtype, const float* w, const int32_t* slot_to_row,
+                          int64_t T, int K, int H, void* out, int out_dtype, hipStream_t stream);
+
+}  // namespace moe

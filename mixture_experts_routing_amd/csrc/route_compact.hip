@@ -1,0 +1,274 @@
+// Route compaction for one expert-parallel rank (gfx950).
+//
+// Source: b70-optimization-lab note "MTP1 M2 compact scheduler closure"
+// (2026-07-16), design paragraph: each local expert's row count and
+// remapped-row prefix are derived on device from topk_ids plus expert_map,
+// the expert-grouped activation layout is kept, duplicates are allowed and a
+// rank whose routes are all remote is valid.
+//
+// Output is a stable counting sort of the slots by local expert id, so every
+// position is fixed by the inputs (no atomics decide an order):
+//   occurrence(s) = number of earlier slots with the same local id
+//   slot_to_row[s] = offsets[l] + occurrence(s)
+// A wavefront takes 64 consecutive slots; the rank of a slot among equal ids
+// of its group comes from a 64-step readlane sweep, and per-wave running
+// counts per expert live in LDS.  A per-expert exclusive prefix over the
+// waves (then over blocks) turns group ranks into occurrences.
+//
+//   N <= kSingleMax : one 1024-thread block does everything (decode sizes)
+//   larger N        : count kernel (per block counts + in-block ranks, which
+//                     are parked in slot_to_row) -> one-block scan kernel
+//                     (per expert prefix over blocks, offsets) -> scatter
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kWaves = 16;
+constexpr int kThreads = kWaves * 64;
+constexpr int kGroupsSingle = 4;                       // 64-slot groups per wave, single-block path
+constexpr int kSingleMax = kWaves * kGroupsSingle * 64;  // 4096 slots
+constexpr int kBlockSlots = kWaves * 64;               // slots per block, multi-block path
+
+__device__ __forceinline__ int local_of(int id, const int32_t* __restrict__ emap, int Eg, int El) {
+  if (id < 0 || id >= Eg) return -1;
+  const int l = emap ? emap[id] : id;
+  return (l >= 0 && l < El) ? l : -1;
+}
+
+// For a group of 64 lanes holding local ids l (-1 = remote/absent): the
+// number of lower lanes with the same id, and the total with that id.
+__device__ __forceinline__ void group_rank(int l, int lane, int& below, int& total) {
+  below = 0;
+  total = 0;
+#pragma unroll 16
+  for (int j = 0; j < 64; ++j) {
+    const int lj = __builtin_amdgcn_readlane(l, j);
+    const int eq = (lj == l) ? 1 : 0;
+    total += eq;
+    below += (j < lane) ? eq : 0;
+  }
+}
+
+// Ranks the 64-slot groups [first_slot + 64*g, ...) of one wave; returns the
+// rank of each lane's slot among equal local ids of this wave's slots (in
+// slot order) and leaves the wave's per-expert totals in run[0..El).
+template <int GPW>
+__device__ __forceinline__ void wave_ranks(const int32_t* __restrict__ ids, int64_t N, int64_t first_slot,
+                                           const int32_t* __restrict__ emap, int Eg, int El, int lane,
+                                           int* __restrict__ run, int (&loc)[GPW], int (&rank)[GPW]) {
+#pragma unroll
+  for (int g = 0; g < GPW; ++g) {
+    const int64_t s0 = first_slot + (int64_t)g * 64;
+    loc[g] = -1;
+    rank[g] = 0;
+    if (s0 >= N) continue;  // uniform
+    const int64_t s = s0 + lane;
+    const int l = (s < N) ? local_of(ids[s], emap, Eg, El) : -1;
+    int below, total;
+    group_rank(l, lane, below, total);
+    if (l >= 0) rank[g] = run[l] + below;
+    // one writer per distinct id: the last occurrence in this group
+    if (l >= 0 && below == total - 1) run[l] += total;
+    loc[g] = l;
+  }
+}
+
+// Exclusive scan of v over the block's threads (kThreads of them); returns
+// the prefix and writes the block total to *total.  tmp: kWaves+1 ints.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += o;
+  }
+  if (lane == 63) tmp[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    const int ws = lane < kWaves ? tmp[lane] : 0;
+    int wi = ws;
+#pragma unroll
+    for (int d = 1; d < kWaves; d <<= 1) {
+      const int o = __shfl_up(wi, d, 64);
+      if (lane >= d) wi += o;
+    }
+    if (lane < kWaves) tmp[lane] = wi - ws;
+    if (lane == kWaves - 1) tmp[kWaves] = wi;
+  }
+  __syncthreads();
+  const int r = tmp[wave] + inc - v;
+  *total = tmp[kWaves];
+  __syncthreads();
+  return r;
+}
+
+// Per-expert exclusive prefix over the kWaves rows of run[w*El + e]; each
+// expert's total goes to cnt[e].
+__device__ __forceinline__ void prefix_over_waves(int* __restrict__ run, int El, int* __restrict__ cnt) {
+  for (int e = threadIdx.x; e < El; e += kThreads) {
+    int acc = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int c = run[w * El + e];
+      run[w * El + e] = acc;
+      acc += c;
+    }
+    cnt[e] = acc;
+  }
+}
+
+// Exclusive scan of cnt[0..El) into offs[0..El]; El <= kThreads.
+__device__ __forceinline__ void scan_counts(const int* __restrict__ cnt, int El, int* __restrict__ offs,
+                                            int* tmp) {
+  const int e = threadIdx.x;
+  const int v = e < El ? cnt[e] : 0;
+  int total;
+  const int ex = block_exclusive_scan(v, tmp, &total);
+  if (e < El) offs[e] = ex;
+  if (e == 0) offs[El] = total;
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// single block: N <= kSingleMax
+
+__global__ __launch_bounds__(kThreads) void compact_single_kernel(
+    const int32_t* __restrict__ ids, int N, const int32_t* __restrict__ emap, int Eg, int El,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ s2r,
+    int32_t* __restrict__ r2s) {
+  extern __shared__ int lds[];
+  int* run = lds;                     // [kWaves][El]
+  int* cnt = run + kWaves * El;       // [El]
+  int* offs = cnt + El;               // [El + 1]
+  int* tmp = offs + El + 1;           // [kWaves + 1]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+  for (int i = threadIdx.x; i < kWaves * El; i += kThreads) run[i] = 0;
+  __syncthreads();
+
+  int loc[kGroupsSingle], rank[kGroupsSingle];
+  const int64_t first = (int64_t)wave * kGroupsSingle * 64;
+  wave_ranks<kGroupsSingle>(ids, N, first, emap, Eg, El, lane, run + wave * El, loc, rank);
+  __syncthreads();
+  prefix_over_waves(run, El, cnt);
+  __syncthreads();
+  scan_counts(cnt, El, offs, tmp);
+
+  for (int e = threadIdx.x; e < El; e += kThreads) counts[e] = cnt[e];
+  for (int e = threadIdx.x; e <= El; e += kThreads) offsets[e] = offs[e];
+
+#pragma unroll
+  for (int g = 0; g < kGroupsSingle; ++g) {
+    const int64_t s = first + g * 64 + lane;
+    if (s < N) {
+      const int l = loc[g];
+      const int row = l >= 0 ? offs[l] + run[wave * El + l] + rank[g] : -1;
+      s2r[s] = row;
+      if (row >= 0) r2s[row] = (int32_t)s;
+    }
+  }
+  const int R = offs[El];
+  for (int r = R + threadIdx.x; r < N; r += kThreads) r2s[r] = -1;
+}
+
+// ---------------------------------------------------------------------------
+// multi block
+
+__global__ __launch_bounds__(kThreads) void compact_count_kernel(
+    const int32_t* __restrict__ ids, int64_t N, const int32_t* __restrict__ emap, int Eg, int El,
+    int32_t* __restrict__ block_counts /*[B][El]*/, int32_t* __restrict__ s2r) {
+  extern __shared__ int lds[];
+  int* run = lds;  // [kWaves][El]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < kWaves * El; i += kThreads) run[i] = 0;
+  __syncthreads();
+  int loc[1], rank[1];
+  const int64_t first = (int64_t)blockIdx.x * kBlockSlots + wave * 64;
+  wave_ranks<1>(ids, N, first, emap, Eg, El, lane, run + wave * El, loc, rank);
+  __syncthreads();
+  prefix_over_waves(run, El, block_counts + (int64_t)blockIdx.x * El);
+  __syncthreads();
+  const int64_t s = first + lane;
+  if (s < N && loc[0] >= 0) s2r[s] = run[wave * El + loc[0]] + rank[0];  // rank inside this block
+}
+
+__global__ __launch_bounds__(kThreads) void compact_scan_kernel(
+    int32_t* __restrict__ block_counts, int B, int El, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets) {
+  extern __shared__ int lds[];
+  int* cnt = lds;           // [El]
+  int* offs = cnt + El;     // [El + 1]
+  int* tmp = offs + El + 1; // [kWaves + 1]
+  for (int e = threadIdx.x; e < El; e += kThreads) {
+    int acc = 0;
+    for (int b = 0; b < B; ++b) {
+      const int c = block_counts[(int64_t)b * El + e];
+      block_counts[(int64_t)b * El + e] = acc;
+      acc += c;
+    }
+    cnt[e] = acc;
+  }
+  __syncthreads();
+  scan_counts(cnt, El, offs, tmp);
+  for (int e = threadIdx.x; e < El; e += kThreads) {
+    counts[e] = cnt[e];
+    const int base = offs[e];
+    for (int b = 0; b < B; ++b) block_counts[(int64_t)b * El + e] += base;
+  }
+  for (int e = threadIdx.x; e <= El; e += kThreads) offsets[e] = offs[e];
+}
+
+__global__ __launch_bounds__(256) void compact_scatter_kernel(
+    const int32_t* __restrict__ ids, int64_t N, const int32_t* __restrict__ emap, int Eg, int El,
+    const int32_t* __restrict__ block_base /*[B][El]*/, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ s2r, int32_t* __restrict__ r2s) {
+  const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (s >= N) return;
+  const int l = local_of(ids[s], emap, Eg, El);
+  int row = -1;
+  if (l >= 0) {
+    const int64_t b = s / kBlockSlots;
+    row = block_base[b * El + l] + s2r[s];
+    r2s[row] = (int32_t)s;
+  }
+  s2r[s] = row;
+  const int R = offsets[El];
+  if (s >= R) r2s[s] = -1;
+}
+
+}  // namespace
+
+size_t route_compact_workspace_bytes(int64_t N, int E_local) {
+  if (N <= kSingleMax) return 0;
+  const int64_t B = (N + kBlockSlots - 1) / kBlockSlots;
+  return (size_t)B * (size_t)E_local * sizeof(int32_t);
+}
+
+hipError_t launch_route_compact(const int32_t* ids, int64_t N, const int32_t* emap, int Eg, int El,
+                                int32_t* counts, int32_t* offsets, int32_t* s2r, int32_t* r2s,
+                                void* workspace, hipStream_t stream) {
+  if (N <= kSingleMax) {
+    const size_t lds = sizeof(int) * ((size_t)kWaves * El + El + El + 1 + kWaves + 1);
+    hipLaunchKernelGGL(compact_single_kernel, dim3(1), dim3(kThreads), lds, stream, ids, (int)N, emap,
+                       Eg, El, counts, offsets, s2r, r2s);
+    return hipGetLastError();
+  }
+  const int64_t B = (N + kBlockSlots - 1) / kBlockSlots;
+  int32_t* bc = static_cast<int32_t*>(workspace);
+  hipLaunchKernelGGL(compact_count_kernel, dim3((unsigned)B), dim3(kThreads),
+                     sizeof(int) * (size_t)kWaves * El, stream, ids, N, emap, Eg, El, bc, s2r);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(compact_scan_kernel, dim3(1), dim3(kThreads),
+                     sizeof(int) * ((size_t)El + El + 1 + kWaves + 1), stream, bc, (int)B, El, counts,
+                     offsets);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(compact_scatter_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, stream,
+                     ids, N, emap, Eg, El, bc, offsets, s2r, r2s);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,312 @@
+// Fused softmax + top-k gate for gfx950.
+//
+// Source: page "Upstream Reference: Deep-Spark xllm + vllm", section "Call
+// Chain: MoE topk_softmax on BI-V100": one fused op turns router logits into
+// routing weights, expert ids and a token-expert index map.  The CUDA kernel
+// named there (one warp-sized group per row, power-of-two expert counts
+// favoured) is prior art only; this kernel is laid out for 64-wide CDNA
+// wavefronts and handles any E up to 1280.
+//
+// Layout: a row of E logits is split over G adjacent lanes of a wavefront
+// (G = 1..64), lane q holding V contiguous experts [q*V, q*V+V), so one
+// wavefront serves 64/G rows and its loads are fully coalesced.  Each logit
+// becomes one integer key that orders by (value desc, index asc):
+//   bf16: int32  (two's-complement of the sign-magnitude value) << 16 | (0xFFFF - j)
+//   f32 : int64  (two's-complement of the sign-magnitude value) << 32 | (0xFFFFFFFF - j)
+// (-0 and +0 map to the same value field, so they tie and the lower index
+// wins).  Keys are unique within a row, so "max" is a single integer max.
+// Each lane sorts its keys (Batcher odd-even merge network, registers only);
+// then K rounds of a DPP group max pick the row's best key and the winning
+// lane pops its head.  The softmax denominator is a fixed-order tree sum of
+// exp2 terms; the K chosen weights use the accurate expf and an IEEE divide.
+#include "moe_internal.h"
+
+#include <limits.h>
+
+namespace moe {
+namespace {
+
+template <typename LT>
+struct Keys;
+
+template <>
+struct Keys<uint16_t> {  // bf16 logits stored as raw bits
+  using Key = int32_t;
+  static constexpr Key kMin = INT32_MIN;  // below every real key
+  __device__ __forceinline__ static Key make(uint32_t bits16, int j) {
+    int32_t mag = (int32_t)(bits16 & 0x7FFFu);
+    int32_t tc = (bits16 & 0x8000u) ? -mag : mag;
+    return (Key)(((uint32_t)tc << 16) | (uint32_t)(0xFFFF - j));
+  }
+  __device__ __forceinline__ static float value(Key k) {
+    int32_t tc = k >> 16;
+    uint32_t bits = tc < 0 ? (0x8000u | (uint32_t)(-tc)) : (uint32_t)tc;
+    return __uint_as_float(bits << 16);
+  }
+  __device__ __forceinline__ static int index(Key k) { return 0xFFFF - (int)(k & 0xFFFF); }
+  __device__ __forceinline__ static float to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+};
+
+template <>
+struct Keys<float> {  // f32 logits, handled through their bits
+  using Key = int64_t;
+  static constexpr Key kMin = INT64_MIN;
+  __device__ __forceinline__ static Key make(uint32_t bits, int j) {
+    int64_t mag = (int64_t)(bits & 0x7FFFFFFFu);
+    int64_t tc = (bits & 0x80000000u) ? -mag : mag;
+    return (Key)(((uint64_t)tc << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j));
+  }
+  __device__ __forceinline__ static float value(Key k) {
+    int64_t tc = k >> 32;
+    uint32_t bits = tc < 0 ? (0x80000000u | (uint32_t)(-tc)) : (uint32_t)tc;
+    return __uint_as_float(bits);
+  }
+  __device__ __forceinline__ static int index(Key k) { return (int)(0xFFFFFFFFu - (uint32_t)k); }
+  __device__ __forceinline__ static float to_f32(uint32_t bits) { return __uint_as_float(bits); }
+};
+
+template <int G, typename Key>
+__device__ __forceinline__ Key group_max(Key k) {
+  if constexpr (sizeof(Key) == 4) return group_max_i32<G>(k);
+  else return group_max_i64<G>(k);
+}
+
+// Descending compare-exchange: larger key to the lower position.
+template <typename Key>
+__device__ __forceinline__ void cx(Key& a, Key& b) {
+  Key hi = a > b ? a : b;
+  Key lo = a > b ? b : a;
+  a = hi;
+  b = lo;
+}
+
+constexpr int pow2_ceil(int n) { int p = 1; while (p < n) p <<= 1; return p; }
+
+// Batcher odd-even merge sort over n registers (padded to a power of two;
+// comparators that touch a padding position are skipped, which is exact
+// because every comparator of this network moves the larger key to the
+// lower position and padding would hold the smallest key).
+template <int N, typename Key>
+__device__ __forceinline__ void sort_desc(Key (&k)[N]) {
+  constexpr int P2 = pow2_ceil(N);
+#pragma unroll
+  for (int p = 1; p < P2; p <<= 1) {
+#pragma unroll
+    for (int kk = p; kk >= 1; kk >>= 1) {
+#pragma unroll
+      for (int j = kk % p; j + kk < P2; j += 2 * kk) {
+#pragma unroll
+        for (int i = 0; i < kk; ++i) {
+          const int a = i + j, b = i + j + kk;
+          if (b < N && (a / (2 * p)) == (b / (2 * p))) cx(k[a], k[b]);
+        }
+      }
+    }
+  }
+}
+
+// Loads the V raw logits [j0, j0+V) of row `row` (bits in uint32 lanes).
+template <typename LT, int V>
+__device__ __forceinline__ void load_row_chunk(const LT* __restrict__ row, int j0, int E, bool vec_ok,
+                                               uint32_t (&raw)[V]) {
+  if constexpr (sizeof(LT) == 2) {
+    static_assert(V % 2 == 0, "bf16 chunks are loaded as pairs");
+    if (vec_ok) {
+      const uint32_t* p = reinterpret_cast<const uint32_t*>(row + j0);
+      if constexpr (V % 8 == 0) {
+#pragma unroll
+        for (int i = 0; i < V / 8; ++i) {
+          u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + i);
+          raw[8 * i + 0] = q.x & 0xFFFFu; raw[8 * i + 1] = q.x >> 16;
+          raw[8 * i + 2] = q.y & 0xFFFFu; raw[8 * i + 3] = q.y >> 16;
+          raw[8 * i + 4] = q.z & 0xFFFFu; raw[8 * i + 5] = q.z >> 16;
+          raw[8 * i + 6] = q.w & 0xFFFFu; raw[8 * i + 7] = q.w >> 16;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < V / 4; ++i) {
+          u32x2 q = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p) + i);
+          raw[4 * i + 0] = q.x & 0xFFFFu; raw[4 * i + 1] = q.x >> 16;
+          raw[4 * i + 2] = q.y & 0xFFFFu; raw[4 * i + 3] = q.y >> 16;
+        }
+        if constexpr (V % 4) {
+          uint32_t q = __builtin_nontemporal_load(p + V / 2 - 1);
+          raw[V - 2] = q & 0xFFFFu;
+          raw[V - 1] = q >> 16;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < V; ++i) raw[i] = (j0 + i < E) ? (uint32_t)row[j0 + i] : 0u;
+    }
+  } else {
+    if (vec_ok && V % 4 == 0) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(row + j0);
+#pragma unroll
+      for (int i = 0; i < V / 4; ++i) {
+        u32x4 q = __builtin_nontemporal_load(p + i);
+        raw[4 * i + 0] = q.x; raw[4 * i + 1] = q.y; raw[4 * i + 2] = q.z; raw[4 * i + 3] = q.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < V; ++i) raw[i] = (j0 + i < E) ? __float_as_uint(row[j0 + i]) : 0u;
+    }
+  }
+}
+
+constexpr int kBlock = 256;
+
+template <typename LT, int G, int V, int KMAX>
+__global__ __launch_bounds__(kBlock) void topk_softmax_kernel(
+    const LT* __restrict__ logits, int64_t T, int E, int K, int renorm, int vec_ok,
+    float* __restrict__ w_out, int32_t* __restrict__ id_out, int32_t* __restrict__ tei_out) {
+  using Tr = Keys<LT>;
+  using Key = typename Tr::Key;
+  constexpr int L = V < KMAX ? V : KMAX;     // keys a lane can ever contribute
+  constexpr int RPL = (KMAX + G - 1) / G;    // output ranks per lane
+  constexpr int ROWS = kBlock / G;
+
+  const int lane_g = threadIdx.x % G;
+  const int64_t t = (int64_t)blockIdx.x * ROWS + threadIdx.x / G;
+  const bool row_ok = t < T;
+  const int j0 = lane_g * V;
+  const bool full = row_ok && (j0 + V <= E);
+
+  uint32_t raw[V];
+  if (row_ok) {
+    load_row_chunk<LT, V>(logits + t * (int64_t)E, j0, E, vec_ok && full, raw);
+  } else {
+#pragma unroll
+    for (int i = 0; i < V; ++i) raw[i] = 0u;
+  }
+
+  Key k[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) k[i] = (row_ok && j0 + i < E) ? Tr::make(raw[i], j0 + i) : Tr::kMin;
+  sort_desc<V>(k);
+
+  // K rounds: the group max is the row's next-best key; its owner pops it.
+  // After round r at most K-1-r more pops follow, so only the first
+  // KMAX-1-r positions of a lane's list still matter.
+  Key top[KMAX];
+#pragma unroll
+  for (int r = 0; r < KMAX; ++r) {
+    if (r < K) {
+      const Key m = group_max<G>(k[0]);
+      top[r] = m;
+      const bool win = (k[0] == m);
+#pragma unroll
+      for (int i = 0; i < L; ++i) {
+        if (i < KMAX - 1 - r) {
+          const Key nxt = (i + 1 < L) ? k[i + 1] : Tr::kMin;
+          k[i] = win ? nxt : k[i];
+        }
+      }
+    } else {
+      top[r] = Tr::kMin;
+    }
+  }
+
+  // softmax denominator: fixed-order pairwise tree inside the lane, then the
+  // DPP group sum
+  const float mx = Tr::value(top[0]);
+  constexpr float kLog2e = 1.4426950408889634f;
+  float ex[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const float v = Tr::to_f32(raw[i]);
+    ex[i] = (row_ok && j0 + i < E) ? __builtin_amdgcn_exp2f((v - mx) * kLog2e) : 0.0f;
+  }
+#pragma unroll
+  for (int w = 1; w < V; w <<= 1) {
+#pragma unroll
+    for (int i = 0; i + w < V; i += 2 * w) ex[i] += ex[i + w];
+  }
+  const float denom = group_sum_f32<G>(ex[0]);
+
+  // each lane finishes ranks lane_g, lane_g + G, ...
+  Key mine[RPL];
+  float e_mine[RPL];
+  float part = 0.0f;
+#pragma unroll
+  for (int c = 0; c < RPL; ++c) {
+    Key kk = Tr::kMin;
+#pragma unroll
+    for (int r = c * G; r < (c + 1) * G && r < KMAX; ++r) kk = (lane_g + c * G == r) ? top[r] : kk;
+    mine[c] = kk;
+    const int q = lane_g + c * G;
+    e_mine[c] = (q < K) ? expf(Tr::value(kk) - mx) : 0.0f;
+    part += e_mine[c];
+  }
+  float norm = denom;
+  if (renorm) norm = group_sum_f32<G>(part);
+
+  if (row_ok) {
+#pragma unroll
+    for (int c = 0; c < RPL; ++c) {
+      const int q = lane_g + c * G;
+      if (q < K) {
+        const int64_t o = t * K + q;
+        w_out[o] = e_mine[c] / norm;
+        id_out[o] = Tr::index(mine[c]);
+        if (tei_out) tei_out[o] = (int32_t)((int64_t)q * T + t);
+      }
+    }
+  }
+}
+
+template <typename LT, int G, int V, int KMAX>
+hipError_t launch_cfg(const LT* logits, int64_t T, int E, int K, int renorm, float* w, int32_t* ids,
+                      int32_t* tei, hipStream_t stream) {
+  constexpr int ROWS = kBlock / G;
+  const int64_t blocks = (T + ROWS - 1) / ROWS;
+  // vector loads need the lane's chunk start aligned: row stride and chunk
+  // size multiples of the vector width, and an aligned base pointer
+  const int elt = (int)sizeof(LT);
+  const int vec_bytes = (elt == 2) ? ((V % 8 == 0) ? 16 : 8) : 16;
+  const bool vec_ok = ((E * elt) % vec_bytes == 0) && ((V * elt) % vec_bytes == 0) &&
+                      ((uintptr_t)logits % vec_bytes == 0);
+  hipLaunchKernelGGL((topk_softmax_kernel<LT, G, V, KMAX>), dim3((unsigned)blocks), dim3(kBlock), 0,
+                     stream, logits, T, E, K, renorm, (int)vec_ok, w, ids, tei);
+  return hipGetLastError();
+}
+
+template <typename LT, int KMAX>
+hipError_t dispatch_gv(const LT* logits, int64_t T, int E, int K, int renorm, float* w, int32_t* ids,
+                       int32_t* tei, hipStream_t stream) {
+#define MOE_GATE_CASE(GG, VV) return launch_cfg<LT, GG, VV, KMAX>(logits, T, E, K, renorm, w, ids, tei, stream)
+  if (E <= 8) MOE_GATE_CASE(1, 8);
+  if (E <= 16) MOE_GATE_CASE(1, 16);
+  if (E <= 20) MOE_GATE_CASE(1, 20);
+  int G = 1;
+  while (G * 20 < E) G <<= 1;
+  const int v = (E + G - 1) / G;  // in (10, 20]
+  const bool v16 = v <= 16;
+  switch (G) {
+    case 2: if (v16) MOE_GATE_CASE(2, 16); MOE_GATE_CASE(2, 20);
+    case 4: if (v16) MOE_GATE_CASE(4, 16); MOE_GATE_CASE(4, 20);
+    case 8: if (v16) MOE_GATE_CASE(8, 16); MOE_GATE_CASE(8, 20);
+    case 16: if (v16) MOE_GATE_CASE(16, 16); MOE_GATE_CASE(16, 20);
+    case 32: if (v16) MOE_GATE_CASE(32, 16); MOE_GATE_CASE(32, 20);
+    case 64: if (v16) MOE_GATE_CASE(64, 16); MOE_GATE_CASE(64, 20);
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_GATE_CASE
+}
+
+}  // namespace
+
+hipError_t launch_topk_softmax(const void* logits, int logits_dtype, int64_t T, int E, int K,
+                               int renormalize, float* w, int32_t* ids, int32_t* tei,
+                               hipStream_t stream) {
+  if (logits_dtype == MOE_BF16) {
+    const uint16_t* p = static_cast<const uint16_t*>(logits);
+    return K <= 8 ? dispatch_gv<uint16_t, 8>(p, T, E, K, renormalize, w, ids, tei, stream)
+                  : dispatch_gv<uint16_t, 32>(p, T, E, K, renormalize, w, ids, tei, stream);
+  }
+  const float* p = static_cast<const float*>(logits);
+  return K <= 8 ? dispatch_gv<float, 8>(p, T, E, K, renormalize, w, ids, tei, stream)
+                : dispatch_gv<float, 32>(p, T, E, K, renormalize, w, ids, tei, stream);
+}
+
+}  // namespace moe

@@ -1,0 +1,94 @@
+"""The C ABI library loads, exports every symbol the public header declares,
+and rejects bad arguments on the host before touching the GPU (CPU only: no
+call here launches a kernel)."""
+import ctypes
+
+import pytest
+import torch
+
+from mixture_experts_routing_amd import _lib
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_every_header_symbol_is_exported(lib):
+    names = _lib.header_symbols()
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures must cover the header exactly"
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert _lib.status_string(0) == "MOE_OK"
+    assert _lib.status_string(1) == "MOE_ERR_INVALID_ARG"
+    assert _lib.status_string(4) == "MOE_ERR_WORKSPACE"
+    assert lib.moe_version().decode().startswith("moe_routing")
+
+
+NULL = None
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+# The validation tests pass fake device pointers that host checks must
+# reject; keep them off machines with a GPU so that a mistake in a test can
+# never reach a kernel launch.
+_no_gpu = pytest.mark.skipif(torch.cuda.device_count() > 0, reason="fake-pointer validation runs only without a GPU")
+
+
+@_no_gpu
+def test_topk_softmax_validation(lib):
+    f = lib.moe_topk_softmax
+    assert f(NULL, 1, 0, 8, 2, 0, NULL, NULL, NULL, NULL) == 0            # T == 0: no-op
+    assert f(FAKE, 1, 4, 8, 9, 0, FAKE, FAKE, NULL, NULL) == 1            # K > E
+    assert f(FAKE, 1, 4, 8, 0, 0, FAKE, FAKE, NULL, NULL) == 1            # K == 0
+    assert f(FAKE, 1, -1, 8, 2, 0, FAKE, FAKE, NULL, NULL) == 1           # T < 0
+    assert f(FAKE, 7, 4, 8, 2, 0, FAKE, FAKE, NULL, NULL) == 2            # bad dtype
+    assert f(FAKE, 1, 4, 2048, 2, 0, FAKE, FAKE, NULL, NULL) == 2         # E too large
+    assert f(FAKE, 1, 4, 64, 33, 0, FAKE, FAKE, NULL, NULL) == 2          # K too large
+    assert f(NULL, 1, 4, 8, 2, 0, FAKE, FAKE, NULL, NULL) == 1            # null logits
+
+
+@_no_gpu
+def test_route_compact_validation(lib):
+    f = lib.moe_route_compact
+    assert f(FAKE, 2, 6, NULL, 256, 40, FAKE, FAKE, FAKE, FAKE, NULL, 0, NULL) == 1   # no map, E_l != E_g
+    assert f(FAKE, 2, 6, FAKE, 32, 40, FAKE, FAKE, FAKE, FAKE, NULL, 0, NULL) == 1    # E_l > E_g
+    assert f(FAKE, 2, 6, FAKE, 4096, 1000, FAKE, FAKE, FAKE, FAKE, NULL, 0, NULL) == 2  # E_l > 768
+    assert f(FAKE, 2, 6, FAKE, 256, 40, NULL, FAKE, FAKE, FAKE, NULL, 0, NULL) == 1   # null counts
+    need = lib.moe_route_compact_workspace_bytes(65536, 8, 128)
+    assert need > 0
+    assert lib.moe_route_compact_workspace_bytes(2, 6, 40) == 0
+    assert f(FAKE, 65536, 8, NULL, 128, 128, FAKE, FAKE, FAKE, FAKE, NULL, 0, NULL) == 4          # workspace
+    assert f(FAKE, 65536, 8, NULL, 128, 128, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, NULL) == 4
+
+
+@_no_gpu
+def test_grouped_ffn_validation(lib):
+    f = lib.moe_grouped_ffn
+    def args(xdt, wdt, H, F, ws=FAKE, wsb=1 << 40, ydt=1, sc=NULL):
+        return (FAKE, xdt, 2, 6, H, F, 40, FAKE, sc, FAKE, sc, wdt, FAKE, FAKE, FAKE, FAKE, ydt, ws, wsb, NULL)
+
+    assert f(*args(0, 1, 4096, 2048)) == 2        # f32 x with bf16 weights
+    assert f(*args(1, 0, 4096, 2048)) == 2        # bf16 x with f32 weights
+    assert f(*args(1, 1, 4001, 2048)) == 2        # H not a multiple of 32
+    assert f(*args(1, 1, 4096, 2048, ydt=2)) == 2  # y as MXFP4
+    assert f(*args(1, 2, 4096, 2048)) == 1        # MXFP4 codes without scales
+    assert f(*args(1, 1, 4096, 2048, ws=NULL)) == 4
+    need = lib.moe_grouped_ffn_workspace_bytes(2, 6, 4096, 2048, 40, 1)
+    assert need == 2 * 6 * 2048 * 2
+    assert f(*args(1, 1, 4096, 2048, wsb=need - 1)) == 4
+    mis = ctypes.c_void_p(0x1002)  # bf16 operands must be 16-byte aligned
+    a = list(args(1, 1, 4096, 2048))
+    a[0] = mis
+    assert f(*a) == 1
+
+
+@_no_gpu
+def test_combine_validation(lib):
+    f = lib.moe_combine
+    assert f(FAKE, 1, FAKE, FAKE, 0, 6, 4096, FAKE, 1, NULL) == 0   # T == 0
+    assert f(FAKE, 2, FAKE, FAKE, 2, 6, 4096, FAKE, 1, NULL) == 2   # y dtype
+    assert f(FAKE, 1, NULL, FAKE, 2, 6, 4096, FAKE, 1, NULL) == 1   # null weights
+    assert f(FAKE, 1, FAKE, FAKE, 2, 0, 4096, FAKE, 1, NULL) == 1   # K == 0

@@ -1,0 +1,98 @@
+"""GPU parity of moe_route_compact against the oracle: counts, offsets and both
+permutations bit-exact, on the seven decode route patterns (x 2 expert maps x
+6 seeds = 84 changed-input cases) and on prefill / MXFP4-decode sized routes."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_routing_amd as moe
+import oracle
+import synth
+from gpu_util import DEV, dev_i32, host_i
+
+pytestmark = pytest.mark.gpu
+
+
+def check_compact(ids, emap, E_local, E_global, tag=""):
+    ids = np.asarray(ids, np.int32)
+    print(f"[compact] {tag} N={ids.size} E_local={E_local}", flush=True)
+    ref = oracle.route_compact(ids, emap, E_local)
+    got = moe.moe_route_compact(dev_i32(ids), None if emap is None else dev_i32(emap), E_local, E_global=E_global)
+    torch.cuda.synchronize()
+    for name, g, r in zip(("counts", "offsets", "slot_to_row", "row_to_slot"), got, ref):
+        g = host_i(g)
+        assert np.array_equal(g, r), f"{tag} {name} differs at {np.flatnonzero(g != r)[:8]}"
+
+
+@pytest.mark.parametrize("pattern", synth.decode_patterns())
+@pytest.mark.parametrize("map_kind", ["contiguous", "random"])
+def test_decode_patterns_84_cases(pattern, map_kind):
+    for seed in range(6):
+        c = synth.decode_case(pattern, map_kind, seed=seed, with_weights=False)
+        check_compact(c.topk_ids, c.expert_map, c.E_local, c.E_global, f"{pattern}/{map_kind}/s{seed}")
+
+
+@pytest.mark.parametrize("T", [2, 16, 64])
+@pytest.mark.parametrize("routes", ["uniform", "all_local"])
+def test_mxfp4_decode_routes(T, routes):
+    c = synth.mxfp4_case(T, routes, seed=0, with_weights=False)
+    check_compact(c.topk_ids, c.expert_map, c.E_local, c.E_global, f"mxfp4 T={T}")
+
+
+@pytest.mark.parametrize("N_tokens,K,Eg,El", [
+    (4096, 8, 128, 128),     # prefill: 32768 slots, multi-block
+    (512, 8, 128, 128),      # 4096 slots: largest single-block size
+    (513, 8, 128, 128),      # 4104 slots: smallest multi-block size
+    (65536, 8, 160, 160),    # 524288 slots
+    (333, 3, 256, 40),
+    (1000, 6, 256, 1),       # one local expert
+    (3000, 8, 1024, 768),    # widest supported local expert set
+])
+def test_random_routes(N_tokens, K, Eg, El):
+    rng = np.random.default_rng(N_tokens + El)
+    ids = rng.integers(0, Eg, size=(N_tokens, K)).astype(np.int32)
+    emap = None if El == Eg else synth.random_expert_map(Eg, El, seed=N_tokens)
+    check_compact(ids, emap, El, Eg, "random")
+
+
+def test_skewed_and_all_remote():
+    rng = np.random.default_rng(5)
+    Eg, El = 256, 32
+    emap = synth.contiguous_expert_map(Eg, El)
+    # every route on one local expert: 8*5000 rows on one expert
+    ids = np.full((5000, 8), 40, np.int32)
+    check_compact(ids, emap, El, Eg, "one-hot")
+    # all remote at prefill size
+    remote = np.flatnonzero(emap < 0)
+    ids = remote[rng.integers(0, remote.size, size=(4096, 8))].astype(np.int32)
+    check_compact(ids, emap, El, Eg, "all-remote-large")
+    # out-of-range ids and map values are remote
+    ids = rng.integers(-3, Eg + 3, size=(50, 4)).astype(np.int32)
+    got = moe.moe_route_compact(dev_i32(ids), dev_i32(emap), El, E_global=Eg)
+    torch.cuda.synchronize()
+    inrange = np.where((ids >= 0) & (ids < Eg), ids, 0)
+    clean = np.where((ids >= 0) & (ids < Eg), ids, remote[0]).astype(np.int32)
+    ref = oracle.route_compact(clean, emap, El)
+    for g, r in zip(got, ref):
+        assert np.array_equal(host_i(g), r)
+    del inrange
+
+
+def test_empty_batch_defines_counts():
+    emap = synth.contiguous_expert_map(256, 40)
+    counts, offsets, s2r, r2s = moe.moe_route_compact(torch.empty((0, 6), dtype=torch.int32, device=DEV),
+                                                      dev_i32(emap), 40, E_global=256)
+    torch.cuda.synchronize()
+    assert host_i(counts).tolist() == [0] * 40
+    assert host_i(offsets).tolist() == [0] * 41
+
+
+def test_deterministic_repeat():
+    rng = np.random.default_rng(9)
+    ids = dev_i32(rng.integers(0, 128, size=(4096, 8)).astype(np.int32))
+    first = [t.clone() for t in moe.moe_route_compact(ids, None, 128)]
+    for _ in range(5):
+        again = moe.moe_route_compact(ids, None, 128)
+        torch.cuda.synchronize()
+        for a, b in zip(first, again):
+            assert torch.equal(a, b)

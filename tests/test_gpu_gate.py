@@ -1,0 +1,108 @@
+"""GPU parity of moe_topk_softmax against the oracle.
+
+ids and token_expert_indices must match bit for bit (ties go to the lower
+expert index); weights within 1e-6 relative (fp32 on the GPU, fp64 oracle).
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_routing_amd as moe
+import oracle
+import synth
+from gpu_util import DEV, dev_any, dev_bf16, dev_f32, host_i
+
+pytestmark = pytest.mark.gpu
+
+W_RTOL = 1e-6
+
+
+def check_gate(logits_host, dtype, K, renorm, tag=""):
+    T, E = logits_host.shape
+    w_ref, ids_ref, tei_ref = oracle.topk_softmax(logits_host, K, renorm, dtype)
+    print(f"[gate] {tag} T={T} E={E} K={K} renorm={renorm} dtype={dtype}", flush=True)
+    w, ids, tei = moe.moe_topk_softmax(dev_any(logits_host, dtype), K, renorm)
+    torch.cuda.synchronize()
+    ids = host_i(ids)
+    bad = np.flatnonzero((ids != ids_ref).any(axis=1))
+    assert bad.size == 0, f"{bad.size} rows differ; first row {bad[:1]}: got {ids[bad[:1]]} want {ids_ref[bad[:1]]}"
+    assert np.array_equal(host_i(tei), tei_ref)
+    w = w.cpu().numpy().astype(np.float64)
+    rel = np.max(np.abs(w - w_ref) / np.abs(w_ref))
+    assert rel <= W_RTOL, f"weights rel err {rel:.3e}"
+    return rel
+
+
+def test_tiny_layer_gate_f32():
+    c = synth.tiny_layer(0)
+    check_gate(c.logits, "f32", c.K, False, "tiny")
+
+
+@pytest.mark.parametrize("E", [128, 160])
+@pytest.mark.parametrize("renorm", [False, True])
+def test_gate_throughput_shapes_full(E, renorm):
+    c = synth.gate_case(E, T=65536, K=8, seed=0, renormalize=renorm)
+    check_gate(c.logits, "bf16", 8, renorm, "full")
+
+
+@pytest.mark.parametrize("E", [1, 2, 3, 5, 8, 13, 16, 17, 20, 21, 33, 40, 64, 100, 128, 160, 200, 256, 384, 512,
+                               1000, 1280])
+def test_gate_expert_counts_bf16(E):
+    rng = np.random.default_rng(E)
+    for K in sorted({1, 2, min(E, 6), min(E, 8), min(E, 9), min(E, 32)}):
+        for T in (1, 7, 333):
+            logits = synth.gate_logits_bf16(T, E, seed=E * 100 + K, tie_fraction=0.3)
+            check_gate(logits, "bf16", K, bool(rng.integers(2)), "sweep")
+
+
+@pytest.mark.parametrize("E", [1, 3, 8, 19, 40, 128, 160, 333])
+def test_gate_expert_counts_f32_with_ties(E):
+    rng = np.random.default_rng(1000 + E)
+    for K in sorted({1, min(E, 2), min(E, 8), min(E, 32)}):
+        # small integer-valued logits: ties everywhere
+        logits = (rng.integers(-4, 5, size=(257, E)) * 0.5).astype(np.float32)
+        check_gate(logits, "f32", K, bool(K % 2), "f32ties")
+        logits = rng.standard_normal((100, E)).astype(np.float32) * 3
+        check_gate(logits, "f32", K, False, "f32normal")
+
+
+def test_gate_special_rows():
+    E, K = 128, 8
+    rows = []
+    rows.append(np.zeros(E, np.float32))                          # all equal -> ids 0..7
+    r = np.full(E, -1.0, np.float32); r[[5, 77]] = 0.0; r[[9]] = -0.0
+    rows.append(r)                                                 # +0 / -0 tie
+    r = np.full(E, -3.0, np.float32); r[E - 8:] = 2.0
+    rows.append(r)                                                 # winners at the end
+    r = np.arange(E, dtype=np.float32)[::-1].copy()
+    rows.append(r)                                                 # strictly decreasing
+    r = np.full(E, 1.0, np.float32); r[0] = 60.0
+    rows.append(r)                                                 # one dominant expert
+    r = np.full(E, -60.0, np.float32); r[3] = 60.0
+    rows.append(r)
+    f = np.stack(rows)
+    check_gate(f, "f32", K, False, "special-f32")
+    check_gate(synth.round_to_bf16_bits(f), "bf16", K, False, "special-bf16")
+    check_gate(synth.round_to_bf16_bits(f), "bf16", K, True, "special-bf16-renorm")
+
+
+def test_gate_deterministic_and_no_overrun():
+    c = synth.gate_case(160, T=4099, K=8, seed=3)
+    x = dev_bf16(c.logits)
+    T, K = 4099, 8
+    # guard words after each output
+    w = torch.full((T * K + 64,), -7.0, dtype=torch.float32, device=DEV)
+    ids = torch.full((T * K + 64,), -7, dtype=torch.int32, device=DEV)
+    tei = torch.full((T * K + 64,), -7, dtype=torch.int32, device=DEV)
+    moe.moe_topk_softmax(x, K, False, w[:T * K].view(T, K), ids[:T * K].view(T, K), tei[:T * K].view(T, K))
+    a = (w.clone(), ids.clone(), tei.clone())
+    moe.moe_topk_softmax(x, K, False, w[:T * K].view(T, K), ids[:T * K].view(T, K), tei[:T * K].view(T, K))
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], w) and torch.equal(a[1], ids) and torch.equal(a[2], tei)
+    assert torch.all(w[T * K:] == -7.0) and torch.all(ids[T * K:] == -7) and torch.all(tei[T * K:] == -7)
+
+
+def test_gate_empty():
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    w, ids, tei = moe.moe_topk_softmax(x, 4, False)
+    assert w.shape == (0, 4)
