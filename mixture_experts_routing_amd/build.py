@@ -21,7 +21,8 @@ LIB_NAME = "libmoe_routing.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["moe_api.hip", "topk_softmax.hip", "route_compact.hip", "grouped_ffn.hip", "combine.hip"]
+SOURCES = ["moe_api.hip", "topk_softmax.hip", "route_compact.hip", "grouped_ffn.hip", "grouped_ffn_tiled.hip",
+           "combine.hip"]
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32
 HIPCC_FLAGS = [

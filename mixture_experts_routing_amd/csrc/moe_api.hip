@@ -98,6 +98,7 @@ int moe_grouped_ffn(const void* x, int x_dtype, int64_t T, int32_t K, int32_t H,
   const size_t need = moe::grouped_ffn_workspace_bytes(T * K, F, w_dtype);
   if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return MOE_ERR_INVALID_ARG;
+  if (!f32_pair && !aligned(y, 16)) return MOE_ERR_INVALID_ARG;  // rows are stored as 16-byte pieces
   return hip_status(moe::launch_grouped_ffn(x, x_dtype, T, K, H, F, E_local, w1, w1_scale, w2, w2_scale, w_dtype,
                                             counts, offsets, row_to_slot, y, y_dtype, workspace,
                                             static_cast<hipStream_t>(stream)));

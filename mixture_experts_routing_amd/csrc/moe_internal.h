@@ -131,6 +131,12 @@ hipError_t launch_grouped_ffn(const void* x, int x_dtype, int64_t T, int K, int 
                               const int32_t* offsets, const int32_t* row_to_slot, void* y,
                               int y_dtype, void* workspace, hipStream_t stream);
 
+// LDS-tiled MFMA path for many rows per expert (bf16 weights)
+bool tiled_ffn_applicable(int64_t N, int H, int F, int El);
+hipError_t launch_tiled_ffn(const uint16_t* x, int64_t T, int64_t N, int topk, int H, int F, int El,
+                            const uint16_t* w1, const uint16_t* w2, const int32_t* counts, const int32_t* offsets,
+                            const int32_t* r2s, void* y, int y_dtype, uint16_t* act, hipStream_t stream);
+
 hipError_t launch_combine(const void* y, int y_dtype, const float* w, const int32_t* slot_to_row,
                           int64_t T, int K, int H, void* out, int out_dtype, hipStream_t stream);
 

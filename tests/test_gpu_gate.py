@@ -28,7 +28,10 @@ def check_gate(logits_host, dtype, K, renorm, tag=""):
     assert bad.size == 0, f"{bad.size} rows differ; first row {bad[:1]}: got {ids[bad[:1]]} want {ids_ref[bad[:1]]}"
     assert np.array_equal(host_i(tei), tei_ref)
     w = w.cpu().numpy().astype(np.float64)
-    rel = np.max(np.abs(w - w_ref) / np.abs(w_ref))
+    # relative bound; weights below the smallest normal float32 (2^-126) may
+    # flush, so they only have to lie within that of the exact value
+    err = np.abs(w - w_ref) - 2.0 ** -126
+    rel = np.max(np.maximum(err, 0.0) / np.abs(w_ref))
     assert rel <= W_RTOL, f"weights rel err {rel:.3e}"
     return rel
 
@@ -49,7 +52,7 @@ def test_gate_throughput_shapes_full(E, renorm):
                                1000, 1280])
 def test_gate_expert_counts_bf16(E):
     rng = np.random.default_rng(E)
-    for K in sorted({1, 2, min(E, 6), min(E, 8), min(E, 9), min(E, 32)}):
+    for K in sorted({min(E, k) for k in (1, 2, 6, 8, 9, 32)}):
         for T in (1, 7, 333):
             logits = synth.gate_logits_bf16(T, E, seed=E * 100 + K, tie_fraction=0.3)
             check_gate(logits, "bf16", K, bool(rng.integers(2)), "sweep")
