@@ -294,6 +294,180 @@ hipError_t dispatch_gv(const LT* logits, int64_t T, int E, int K, int renorm, fl
 #undef MOE_GATE_CASE
 }
 
+
+// ---------------------------------------------------------------------------
+// Fast path: bf16 logits, K <= 8, E = 8*V with V in {8, 12, 16, 20, 24}, rows
+// 16-byte (V % 8 == 0) or 8-byte aligned.  Eight lanes per row (32 rows per
+// 256-thread block), no bounds checks in the body, keys built two at a time
+// with packed 16-bit ALU ops, and only each lane's top 8 keys kept (two or
+// three sorting networks and bitonic merges instead of a full sort).
+
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// descending Batcher sort of 8 registers (19 comparators)
+__device__ __forceinline__ void sort8_desc(int32_t* k) {
+  cx(k[0], k[1]); cx(k[2], k[3]); cx(k[4], k[5]); cx(k[6], k[7]);
+  cx(k[0], k[2]); cx(k[1], k[3]); cx(k[4], k[6]); cx(k[5], k[7]);
+  cx(k[1], k[2]); cx(k[5], k[6]);
+  cx(k[0], k[4]); cx(k[1], k[5]); cx(k[2], k[6]); cx(k[3], k[7]);
+  cx(k[2], k[4]); cx(k[3], k[5]);
+  cx(k[1], k[2]); cx(k[3], k[4]); cx(k[5], k[6]);
+}
+// descending sort of 4 registers (5 comparators)
+__device__ __forceinline__ void sort4_desc(int32_t* k) {
+  cx(k[0], k[1]); cx(k[2], k[3]); cx(k[0], k[2]); cx(k[1], k[3]); cx(k[1], k[2]);
+}
+// a[0..8) sorted desc <- top 8 of (a, b), b[0..nb) sorted desc (nb <= 8):
+// max(a[i], b[7-i]) is a bitonic sequence holding the 8 largest; a
+// half-cleaner network then sorts it.
+__device__ __forceinline__ void merge_top8(int32_t* a, const int32_t* b, int nb) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int j = 7 - i;
+    if (j < nb) a[i] = max(a[i], b[j]);
+  }
+  cx(a[0], a[4]); cx(a[1], a[5]); cx(a[2], a[6]); cx(a[3], a[7]);
+  cx(a[0], a[2]); cx(a[1], a[3]); cx(a[4], a[6]); cx(a[5], a[7]);
+  cx(a[0], a[1]); cx(a[2], a[3]); cx(a[4], a[5]); cx(a[6], a[7]);
+}
+
+template <int V>
+__global__ __launch_bounds__(kBlock) void topk8_bf16_kernel(const uint16_t* __restrict__ logits, int64_t T, int K,
+                                                            int renorm, float* __restrict__ w_out,
+                                                            int32_t* __restrict__ id_out,
+                                                            int32_t* __restrict__ tei_out) {
+  constexpr int G = 8, E = G * V, W = V / 2;  // W: 32-bit words per lane
+  const int q = threadIdx.x & 7;
+  const int64_t t = (int64_t)blockIdx.x * (kBlock / G) + (threadIdx.x >> 3);
+  const bool row_ok = t < T;
+  const int64_t tc = row_ok ? t : 0;  // out-of-range rows read row 0, store nothing
+
+  uint32_t wd[W];
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(logits + tc * E + q * V);
+  if constexpr (V % 8 == 0) {
+#pragma unroll
+    for (int i = 0; i < W / 4; ++i) {
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + i);
+      wd[4 * i] = v.x; wd[4 * i + 1] = v.y; wd[4 * i + 2] = v.z; wd[4 * i + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < W / 2; ++i) {
+      const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src) + i);
+      wd[2 * i] = v.x; wd[2 * i + 1] = v.y;
+    }
+  }
+
+  // keys: (two's-complement value << 16) | (0xFFFF - index), two per word.
+  // sign-magnitude -> two's complement per 16-bit half: (mag ^ s) - s with
+  // s = 0 or -1; -0 becomes 0.
+  int32_t key[V];
+  const int j0 = q * V;
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    const s16x2 h = __builtin_bit_cast(s16x2, wd[i]);
+    const s16x2 sg = h >> (s16x2){15, 15};
+    const s16x2 mag = __builtin_bit_cast(s16x2, wd[i] & 0x7FFF7FFFu);
+    const uint32_t tcv = __builtin_bit_cast(uint32_t, (s16x2)((mag ^ sg) - sg));
+    key[2 * i] = (int32_t)((tcv << 16) | (uint32_t)(0xFFFF - (j0 + 2 * i)));
+    key[2 * i + 1] = (int32_t)((tcv & 0xFFFF0000u) | (uint32_t)(0xFFFF - (j0 + 2 * i + 1)));
+  }
+
+  // this lane's 8 best keys, sorted
+  int32_t k[8];
+  if constexpr (V == 8) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) k[i] = key[i];
+    sort8_desc(k);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) k[i] = key[i];
+    sort8_desc(k);
+    if constexpr (V >= 16) {
+      sort8_desc(key + 8);
+      merge_top8(k, key + 8, 8);
+    }
+    if constexpr (V == 12 || V == 20) {
+      sort4_desc(key + V - 4);
+      merge_top8(k, key + V - 4, 4);
+    }
+    if constexpr (V == 24) {
+      sort8_desc(key + 16);
+      merge_top8(k, key + 16, 8);
+    }
+  }
+
+  // K rounds of an 8-lane max; the owner pops.  After round r only the first
+  // 7-r entries can still be needed.
+  int32_t top[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    if (r < K) {
+      const int32_t m = group_max_i32<G>(k[0]);
+      top[r] = m;
+      const bool win = (k[0] == m);
+#pragma unroll
+      for (int i = 0; i < 7 - r; ++i) k[i] = win ? k[i + 1] : k[i];
+    } else {
+      top[r] = INT32_MIN;
+    }
+  }
+
+  // softmax denominator over the lane's V values, pairwise, then the group
+  const float mx = Keys<uint16_t>::value(top[0]);
+  constexpr float kLog2e = 1.4426950408889634f;
+  float ex[V];
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    ex[2 * i] = __builtin_amdgcn_exp2f((__uint_as_float(wd[i] << 16) - mx) * kLog2e);
+    ex[2 * i + 1] = __builtin_amdgcn_exp2f((__uint_as_float(wd[i] & 0xFFFF0000u) - mx) * kLog2e);
+  }
+#pragma unroll
+  for (int w = 1; w < V; w <<= 1) {
+#pragma unroll
+    for (int i = 0; i + w < V; i += 2 * w) ex[i] += ex[i + w];
+  }
+  const float denom = group_sum_f32<G>(ex[0]);
+
+  // lane q finishes rank q
+  int32_t mine = top[0];
+#pragma unroll
+  for (int r = 1; r < 8; ++r) mine = (q == r) ? top[r] : mine;
+  const float e = (q < K) ? expf(Keys<uint16_t>::value(mine) - mx) : 0.0f;
+  const float norm = renorm ? group_sum_f32<G>(e) : denom;
+  if (row_ok && q < K) {
+    const int64_t o = t * K + q;
+    w_out[o] = e / norm;
+    id_out[o] = Keys<uint16_t>::index(mine);
+    if (tei_out) tei_out[o] = (int32_t)((int64_t)q * T + t);
+  }
+}
+
+template <int V>
+hipError_t launch_fast(const uint16_t* logits, int64_t T, int K, int renorm, float* w, int32_t* ids, int32_t* tei,
+                       hipStream_t stream) {
+  const int64_t blocks = (T + (kBlock / 8) - 1) / (kBlock / 8);
+  hipLaunchKernelGGL((topk8_bf16_kernel<V>), dim3((unsigned)blocks), dim3(kBlock), 0, stream, logits, T, K, renorm, w,
+                     ids, tei);
+  return hipGetLastError();
+}
+
+// E = 8*V with V in {8, 12, 16, 20, 24}, K <= 8, aligned rows: the fast kernel
+bool try_fast(const uint16_t* logits, int64_t T, int E, int K, int renorm, float* w, int32_t* ids, int32_t* tei,
+              hipStream_t stream, hipError_t* err) {
+  if (K > 8 || E % 8 != 0) return false;
+  const int V = E / 8;
+  const int align = (V % 8 == 0) ? 16 : 8;
+  if ((uintptr_t)logits % align != 0 || (E * 2) % align != 0) return false;
+  switch (V) {
+    case 8: *err = launch_fast<8>(logits, T, K, renorm, w, ids, tei, stream); return true;
+    case 12: *err = launch_fast<12>(logits, T, K, renorm, w, ids, tei, stream); return true;
+    case 16: *err = launch_fast<16>(logits, T, K, renorm, w, ids, tei, stream); return true;
+    case 20: *err = launch_fast<20>(logits, T, K, renorm, w, ids, tei, stream); return true;
+    case 24: *err = launch_fast<24>(logits, T, K, renorm, w, ids, tei, stream); return true;
+    default: return false;
+  }
+}
 }  // namespace
 
 hipError_t launch_topk_softmax(const void* logits, int logits_dtype, int64_t T, int E, int K,
@@ -301,6 +475,8 @@ hipError_t launch_topk_softmax(const void* logits, int logits_dtype, int64_t T, 
                                hipStream_t stream) {
   if (logits_dtype == MOE_BF16) {
     const uint16_t* p = static_cast<const uint16_t*>(logits);
+    hipError_t err;
+    if (try_fast(p, T, E, K, renormalize, w, ids, tei, stream, &err)) return err;
     return K <= 8 ? dispatch_gv<uint16_t, 8>(p, T, E, K, renormalize, w, ids, tei, stream)
                   : dispatch_gv<uint16_t, 32>(p, T, E, K, renormalize, w, ids, tei, stream);
   }
