@@ -20,7 +20,9 @@ Besides the contract fields the line carries:
   secondary     gate throughput (65536 rows, E=128 and 160, bf16) in Mrows/s
                 and %-of-HBM with rotating buffers larger than the 256 MB
                 last-level cache; decode layer (M=2, top-6, 40 local
-                experts) per route pattern with achieved weight-stream GB/s
+                experts) per route pattern with achieved weight-stream GB/s.
+                Both are short calls, timed from HIP-graph replays so that
+                host launch overhead is not counted.
 """
 from __future__ import annotations
 
@@ -72,6 +74,32 @@ def f32_dev(a, dev):
     import torch
 
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+
+def graph_ms(fn, reps, dev):
+    """Milliseconds per fn() call on the GPU, without host launch overhead:
+    fn() (a fixed sequence of library calls on the current stream) is captured
+    once in a HIP graph, and the graph is replayed `reps` times between two
+    events.  The calls hold no allocation and no memset, so they capture."""
+    import torch
+
+    fn()  # eager warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    g.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(reps):
+        g.replay()
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del g
+    return ms
 
 
 # ---------------------------------------------------------------------------
@@ -144,7 +172,7 @@ def bench_prefill(args, dev):
     roofline = {
         "bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
         "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic_for("grouped_ffn_prefill"),
-        "kernel": "moe_grouped_ffn (ffn1_stream_kernel + ffn2_stream_kernel)",
+        "kernel": "moe_grouped_ffn (ffn_tiled_kernel: GEMM1 + silu_and_mul, then GEMM2)",
         "algorithmic_flops_per_launch": flops, "avg_launch_ms": round(per["grouped_ffn"], 4),
     }
     log(f"[bench] prefill layer: {ms_per_step:.3f} ms/step, {T / (ms_per_step / 1e3):.0f} tokens/s; "
@@ -193,18 +221,12 @@ def bench_gate(dev, E, reps):
         lb = bf16_dev(base, dev).roll(i, dims=0).contiguous()
         bufs.append((lb, torch.empty((T, K), dtype=torch.float32, device=dev),
                      torch.empty((T, K), dtype=torch.int32, device=dev), torch.empty((T, K), dtype=torch.int32, device=dev)))
-    stream = torch.cuda.current_stream(dev)
-    for b in bufs:
-        moe.moe_topk_softmax(b[0], K, False, b[1], b[2], b[3], stream=stream)
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for r in range(reps):
-        b = bufs[r % nbuf]
-        moe.moe_topk_softmax(b[0], K, False, b[1], b[2], b[3], stream=stream)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / reps
+
+    def calls():
+        for b in bufs:
+            moe.moe_topk_softmax(b[0], K, False, b[1], b[2], b[3])
+
+    ms = graph_ms(calls, max(1, reps // nbuf), dev) / nbuf
     nbytes = T * E * 2 + T * K * 12
     gbs = nbytes / (ms / 1e3) / 1e9
     return {"E": E, "T": T, "K": K, "ms": round(ms, 5), "mrows_per_s": round(T / (ms / 1e3) / 1e6, 1),
@@ -230,7 +252,6 @@ def bench_decode(dev, reps):
     emap = synth.contiguous_expert_map(Eg, El)
     emap_d = i32_dev(emap, dev)
     inv = np.flatnonzero(emap >= 0)  # local -> global under the contiguous map
-    stream = torch.cuda.current_stream(dev)
     res = {}
     nvar = 8  # rotated copies of each pattern: consecutive calls touch different experts
     for pat in synth.decode_patterns():
@@ -243,37 +264,37 @@ def bench_decode(dev, reps):
             ids = np.array([[int(inv[l]) if l is not None else int(base.topk_ids[t, k])
                              for k, l in enumerate(r)] for t, r in enumerate(rows)], dtype=np.int32)
             variants.append(i32_dev(ids, dev))
-        outs = (torch.empty(El, dtype=torch.int32, device=dev), torch.empty(El + 1, dtype=torch.int32, device=dev),
-                torch.empty(T * K, dtype=torch.int32, device=dev), torch.empty(T * K, dtype=torch.int32, device=dev))
+        # one set of compaction outputs per variant, so each phase can be
+        # captured and timed on its own
+        outs = [(torch.empty(El, dtype=torch.int32, device=dev), torch.empty(El + 1, dtype=torch.int32, device=dev),
+                 torch.empty(T * K, dtype=torch.int32, device=dev), torch.empty(T * K, dtype=torch.int32, device=dev))
+                for _ in range(nvar)]
         fws = torch.empty(moe.grouped_ffn_workspace_bytes(T, K, H, F, El, moe.MOE_BF16), dtype=torch.uint8,
                           device=dev)
         y = torch.empty((T * K, H), dtype=torch.bfloat16, device=dev)
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
 
-        def layer(ids, ev=None):
-            if ev:
-                ev[0].record(stream)
-            counts, offsets, s2r, r2s = moe.moe_route_compact(ids, emap_d, El, E_global=Eg, out=outs, stream=stream)
-            if ev:
-                ev[1].record(stream)
-            moe.moe_grouped_ffn(x, K, w1, w2, counts, offsets, r2s, y=y, workspace=fws, stream=stream)
-            if ev:
-                ev[2].record(stream)
-            moe.moe_combine(y, tw, s2r, out=out, stream=stream)
-            if ev:
-                ev[3].record(stream)
+        def compact(v):
+            moe.moe_route_compact(variants[v], emap_d, El, E_global=Eg, out=outs[v])
 
-        for v in range(nvar):
-            layer(variants[v])
-        torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
-        for r in range(reps):
-            layer(variants[r % nvar], evs[r])
-        torch.cuda.synchronize()
-        t_layer = sum(e[0].elapsed_time(e[3]) for e in evs) / reps
-        t_cmp = sum(e[0].elapsed_time(e[1]) for e in evs) / reps
-        t_ffn = sum(e[1].elapsed_time(e[2]) for e in evs) / reps
-        t_cmb = sum(e[2].elapsed_time(e[3]) for e in evs) / reps
+        def ffn(v):
+            counts, offsets, _, r2s = outs[v]
+            moe.moe_grouped_ffn(x, K, w1, w2, counts, offsets, r2s, y=y, workspace=fws)
+
+        def combine(v):
+            moe.moe_combine(y, tw, outs[v][2], out=out)
+
+        def each(*fns):
+            def run():
+                for v in range(nvar):
+                    for f in fns:
+                        f(v)
+            return run
+
+        t_cmp = graph_ms(each(compact), reps, dev) / nvar
+        t_ffn = graph_ms(each(ffn), reps, dev) / nvar
+        t_cmb = graph_ms(each(combine), reps, dev) / nvar
+        t_layer = graph_ms(each(compact, ffn, combine), reps, dev) / nvar
         n_exp = len({l for r in synth.DECODE_PATTERNS[pat] for l in r if l is not None})
         wbytes = n_exp * (2 * F * H + H * F) * 2
         d = {"layer_ms": round(t_layer, 4), "compact_ms": round(t_cmp, 4), "ffn_ms": round(t_ffn, 4),
@@ -333,7 +354,7 @@ def main():
         for g in secondary["gate"]:
             log(f"[bench] gate E={g['E']}: {g['ms'] * 1e3:.2f} us, {g['mrows_per_s']} Mrows/s, "
                 f"{g['gbs']} GB/s ({100 * g['hbm_frac']:.1f}% of HBM)")
-        secondary["decode"] = bench_decode(dev, 16 if args.quick else 80)
+        secondary["decode"] = bench_decode(dev, 5 if args.quick else 20)
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")

@@ -125,8 +125,10 @@ size_t moe_route_compact_workspace_bytes(int64_t T, int32_t K, int32_t E_local);
  *   y (out)  [T*K, H] (y_dtype MOE_F32 or MOE_BF16); rows >= R are not written
  * Supported (x, w) pairs: (F32, F32), (BF16, BF16), (BF16, MXFP4).
  * The intermediate act is kept in the workspace in bf16 for bf16/MXFP4
- * weights and in fp32 for fp32 weights.
- * workspace: moe_grouped_ffn_workspace_bytes(...) bytes of device scratch.
+ * weights and in fp32 for fp32 weights.  Every sum is taken in a fixed
+ * order, so results are deterministic for a given input.
+ * workspace: moe_grouped_ffn_workspace_bytes(...) bytes of device scratch,
+ * 16-byte aligned.
  * Limits: H and F multiples of 32 for bf16/MXFP4 (of 1 for f32); H, F >= 1.
  */
 int moe_grouped_ffn(const void* x, int x_dtype, int64_t T, int32_t K, int32_t H, int32_t F,

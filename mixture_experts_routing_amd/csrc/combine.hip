@@ -4,11 +4,11 @@
 //
 //   out[t, :] = sum_{k ascending, slot_to_row[t*K+k] >= 0} w[t,k] * y[row, :]
 //
-// One block per token; each thread owns 8 consecutive hidden elements (one
-// 16-byte load of a bf16 row) and walks the token's K slots in order, so the
-// fp32 accumulation order is fixed.  Slot rows and weights are wave-uniform
-// and come through the scalar cache.  HBM-bound: it reads R*H elements of y
-// and writes T*H outputs.
+// A block covers one token and 2048 hidden elements; each thread owns 8
+// consecutive elements (one 16-byte load of a bf16 row) and adds the token's
+// K slots in ascending k, so the fp32 accumulation order is fixed.  Slot rows
+// and weights are block-uniform and come through the scalar cache.
+// HBM-bound: it reads R*H elements of y and writes T*H outputs.
 #include "moe_internal.h"
 
 namespace moe {
@@ -56,7 +56,12 @@ __device__ __forceinline__ void store1(OT* p, float v) {
   else *p = v;
 }
 
-// YT/OT: uint16_t (bf16 bits) or float
+// YT/OT: uint16_t (bf16 bits) or float.  Block (t, c): token t, hidden
+// elements [c*kThreads*EPT, ...).  Slots are taken kSlotChunk at a time: the
+// rows of the chunk are all requested before the first FMA, then added in
+// ascending k, so K dependent memory round trips become one per chunk.
+constexpr int kSlotChunk = 8;
+
 template <typename YT, typename OT, bool VEC>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const YT* __restrict__ y, const float* __restrict__ w,
                                                           const int32_t* __restrict__ s2r, int64_t T, int K,
@@ -64,31 +69,37 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const YT* __restrict_
   const int64_t t = blockIdx.x;
   const int32_t* rows = s2r + t * K;
   const float* wt = w + t * K;
-  if constexpr (VEC) {
-    for (int c = threadIdx.x * 8; c < H; c += kThreads * 8) {
-      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int k = 0; k < K; ++k) {
-        const int r = rows[k];
-        if (r < 0) continue;
-        const float wk = wt[k];
-        float v[8];
-        load8(y + (int64_t)r * H + c, v);
+  constexpr int EPT = VEC ? 8 : 1;  // elements per thread
+  const int c = (blockIdx.y * kThreads + threadIdx.x) * EPT;
+  if (c >= H) return;
+  float acc[EPT];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wk, v[i], acc[i]);
-      }
-      store8(out + t * H + c, acc);
+  for (int i = 0; i < EPT; ++i) acc[i] = 0.0f;
+  for (int k0 = 0; k0 < K; k0 += kSlotChunk) {
+    int r[kSlotChunk];
+    float wk[kSlotChunk], v[kSlotChunk][EPT];
+#pragma unroll
+    for (int j = 0; j < kSlotChunk; ++j) {
+      r[j] = (k0 + j < K) ? rows[k0 + j] : -1;
+      wk[j] = (k0 + j < K) ? wt[k0 + j] : 0.0f;
     }
-  } else {
-    for (int c = threadIdx.x; c < H; c += kThreads) {
-      float acc = 0.0f;
-      for (int k = 0; k < K; ++k) {
-        const int r = rows[k];
-        if (r < 0) continue;
-        acc = fmaf(wt[k], load1(y + (int64_t)r * H + c), acc);
+#pragma unroll
+    for (int j = 0; j < kSlotChunk; ++j) {
+      if (r[j] >= 0) {
+        if constexpr (VEC) load8(y + (int64_t)r[j] * H + c, v[j]);
+        else v[j][0] = load1(y + (int64_t)r[j] * H + c);
       }
-      store1(out + t * H + c, acc);
+    }
+#pragma unroll
+    for (int j = 0; j < kSlotChunk; ++j) {
+      if (r[j] >= 0) {
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) acc[i] = fmaf(wk[j], v[j][i], acc[i]);
+      }
     }
   }
+  if constexpr (VEC) store8(out + t * H + c, acc);
+  else store1(out + t * H + c, acc[0]);
 }
 
 template <typename YT, typename OT>
@@ -97,12 +108,12 @@ hipError_t launch_typed(const void* y, const float* w, const int32_t* s2r, int64
   const YT* yp = static_cast<const YT*>(y);
   OT* op = static_cast<OT*>(out);
   const bool vec = (H % 8 == 0) && ((uintptr_t)y % 16 == 0) && ((uintptr_t)out % 16 == 0);
+  const int per_block = kThreads * (vec ? 8 : 1);
+  const dim3 grid((unsigned)T, (unsigned)((H + per_block - 1) / per_block));
   if (vec)
-    hipLaunchKernelGGL((combine_kernel<YT, OT, true>), dim3((unsigned)T), dim3(kThreads), 0, stream, yp, w, s2r,
-                       T, K, H, op);
+    hipLaunchKernelGGL((combine_kernel<YT, OT, true>), grid, dim3(kThreads), 0, stream, yp, w, s2r, T, K, H, op);
   else
-    hipLaunchKernelGGL((combine_kernel<YT, OT, false>), dim3((unsigned)T), dim3(kThreads), 0, stream, yp, w, s2r,
-                       T, K, H, op);
+    hipLaunchKernelGGL((combine_kernel<YT, OT, false>), grid, dim3(kThreads), 0, stream, yp, w, s2r, T, K, H, op);
   return hipGetLastError();
 }
 

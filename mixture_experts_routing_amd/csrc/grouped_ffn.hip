@@ -65,6 +65,55 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ counts, co
   return false;
 }
 
+// Number of M-tiles of height BM over all experts (wave-uniform).
+__device__ __forceinline__ int count_tiles(const int32_t* __restrict__ counts, int El, int BM) {
+  const int lane = threadIdx.x & 63;
+  int n = 0;
+  for (int c0 = 0; c0 < El; c0 += 64) {
+    const int ee = c0 + lane;
+    n += ee < El ? (counts[ee] + BM - 1) / BM : 0;
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) n += __shfl_xor(n, d, 64);
+  return n;
+}
+
+// Tile table of up to 64 experts held in one wave's registers (lane = local
+// expert): counts and offsets are read once, side by side, so looking up a
+// tile costs no further memory round trip.
+struct TileTab {
+  int cnt, off, nt, incl, total;
+};
+
+__device__ __forceinline__ TileTab load_tile_tab(const int32_t* __restrict__ counts,
+                                                 const int32_t* __restrict__ offsets, int El, int BM) {
+  const int lane = threadIdx.x & 63;
+  TileTab t;
+  t.cnt = lane < El ? counts[lane] : 0;
+  t.off = lane < El ? offsets[lane] : 0;
+  t.nt = (t.cnt + BM - 1) / BM;
+  int inc = t.nt;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += o;
+  }
+  t.incl = inc;
+  t.total = __shfl(inc, 63, 64);
+  return t;
+}
+
+// Tile i (< t.total): expert, first grouped row, valid rows (wave-uniform).
+__device__ __forceinline__ void tab_find(const TileTab& t, int BM, int i, int& e, int& row0, int& nrows) {
+  const bool own = (i >= t.incl - t.nt) && (i < t.incl);
+  const unsigned long long m = __ballot(own);
+  const int src = __ffsll((long long)m) - 1;
+  e = src;
+  const int tile_in_e = i - __shfl(t.incl - t.nt, src, 64);
+  row0 = __shfl(t.off, src, 64) + tile_in_e * BM;
+  nrows = min(BM, __shfl(t.cnt, src, 64) - tile_in_e * BM);
+}
+
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
 
 // One lane's KS/4-element slice of a bf16 row, as KS/32 MFMA operands.
@@ -240,6 +289,267 @@ __global__ __launch_bounds__(kThreads) void ffn2_stream_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Few rows per expert (decode): 16-wave blocks with an in-block K split.
+//
+// With a handful of rows per expert the FFN is a weight stream.  One wave per
+// 16 output columns of a 16-row M-tile leaves too few waves in flight to keep
+// HBM busy when only one or two experts are hit, so each 1024-thread block
+// takes an item -- one M-tile and 16/S groups of 16 columns -- and its 16
+// waves split the reduction dimension S ways.  The partial accumulators meet
+// in LDS and are summed in split order, so the result does not depend on
+// timing.  S is derived on device from the actual tile count so that about
+// kDecodeWaves waves have work, and the grid is persistent: a fixed number of
+// blocks walks the item list, so nothing is launched for tiles that do not
+// exist (an all-remote batch costs one pass over counts).
+//
+// K is walked in 32-wide units; in unit u, lane group g = lane/16 holds
+// elements [32u + 8g, 32u + 8g + 8) of its A row and B row (the same K
+// assignment on both operands, as the MFMA sum requires), so one load
+// instruction reads 64 contiguous bytes of each of 16 weight rows.
+
+constexpr int kDecThreads = 1024;
+constexpr int kDecWaves = kDecThreads / 64;
+constexpr int kDecodeWaves = 4096;  // 16 waves on each of 256 compute units
+constexpr int kDecGrid = 256;
+// K units loaded before their MFMAs: 8 (512 bytes of each bf16 weight row);
+// 4 for MXFP4 GEMM1, whose widened operands would not fit in 128 VGPRs at 8
+template <bool MX>
+constexpr int dec_unroll1() { return MX ? 4 : 8; }
+constexpr int kDecUnroll = 8;
+
+__device__ __forceinline__ int floor_pow2(int v) { return 1 << (31 - __clz(v)); }
+
+// K split: the largest power of two <= 16 that gives each split at least one
+// K unit and keeps the waves with work near kDecodeWaves.
+__device__ __forceinline__ int decode_split(int tiles, int col_groups, int units) {
+  const int64_t work = (int64_t)tiles * col_groups;  // waves with work when S = 1
+  int s = work >= kDecodeWaves ? 1 : floor_pow2((int)(kDecodeWaves / (work > 0 ? work : 1)));
+  s = min(s, kDecWaves);
+  return min(s, floor_pow2(units));
+}
+
+__device__ __forceinline__ bf16x8 widen_mx8(uint32_t w, uint32_t e8) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const float s = e8 == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(e8 << 23);
+  bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0);
+  bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1);
+  bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2);
+  bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3);
+  return bf16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+__device__ __forceinline__ bf16x8 unit_bf16(const uint16_t* __restrict__ row, int u, int g) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + 32 * u + 8 * g));
+}
+
+// Raw pieces of one K unit of a weight row: bf16 -> 16 bytes; MXFP4 -> the
+// 4 code bytes of this lane and the unit's scale byte.
+template <bool MX>
+struct WUnit;
+template <>
+struct WUnit<false> {
+  u32x4 v;
+  __device__ __forceinline__ void load(const void* __restrict__ w, const uint8_t* __restrict__, int64_t row,
+                                       int kdim, int u, int g) {
+    v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(w) + row * kdim + 32 * u + 8 * g);
+  }
+  __device__ __forceinline__ bf16x8 get() const { return __builtin_bit_cast(bf16x8, v); }
+};
+template <>
+struct WUnit<true> {
+  uint32_t c, e8;
+  __device__ __forceinline__ void load(const void* __restrict__ w, const uint8_t* __restrict__ ws, int64_t row,
+                                       int kdim, int u, int g) {
+    c = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(w) + row * (kdim / 2) + 16 * u + 4 * g);
+    e8 = ws[row * (kdim / 32) + u];
+  }
+  __device__ __forceinline__ bf16x8 get() const { return widen_mx8(c, e8); }
+};
+
+// GEMM1 + silu_and_mul for the decode regime.  Same operands as
+// ffn1_stream_kernel.
+template <bool MX>
+__global__ __launch_bounds__(kDecThreads) void ffn1_decode_kernel(
+    const uint16_t* __restrict__ x, int K, int H, int F, int El, const void* __restrict__ w1,
+    const uint8_t* __restrict__ w1s, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ r2s, uint16_t* __restrict__ act) {
+  constexpr int U = dec_unroll1<MX>();
+  __shared__ float red[kDecWaves][8][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  const bool small = El <= 64;  // uniform
+  TileTab tab{};
+  if (small) tab = load_tile_tab(counts, offsets, El, 16);
+  const int tiles = small ? tab.total : count_tiles(counts, El, 16);
+  const int CG = F / 16, units = H / 32;
+  const int S = decode_split(tiles, CG, units);
+  const int cpb = kDecWaves / S;         // column groups per item
+  const int ipt = (CG + cpb - 1) / cpb;  // items per tile
+  const int items = tiles * ipt;
+  const int ks = wave % S, cgl = wave / S;
+  const int per = (units + S - 1) / S;
+  const int u_begin = min(units, ks * per), u_end = min(units, u_begin + per);
+
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int tile = it / ipt, cb = it % ipt;
+    int e = 0, row0 = 0, nrows = 0;
+    if (small) tab_find(tab, 16, tile, e, row0, nrows);
+    else find_tile(counts, offsets, El, 16, tile, e, row0, nrows);
+    const int cg = cb * cpb + cgl;
+    const bool active = cg < CG;
+    f32x4 ag = {0, 0, 0, 0}, au = {0, 0, 0, 0};
+    if (active) {
+      // rows past the tile's end reuse the first row; their results are dropped
+      const int tok = r2s[row0 + (c < nrows ? c : 0)] / K;
+      const uint16_t* xr = x + (int64_t)tok * H;
+      const int64_t rg = (int64_t)e * 2 * F + cg * 16 + c, ru = rg + F;
+      int u = u_begin;
+      for (; u + U <= u_end; u += U) {
+        WUnit<MX> bg[U], bu[U];
+        bf16x8 a[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+          bg[j].load(w1, w1s, rg, H, u + j, g);
+          bu[j].load(w1, w1s, ru, H, u + j, g);
+        }
+#pragma unroll
+        for (int j = 0; j < U; ++j) a[j] = unit_bf16(xr, u + j, g);
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+          ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], bg[j].get(), ag, 0, 0, 0);
+          au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], bu[j].get(), au, 0, 0, 0);
+        }
+      }
+      for (; u < u_end; ++u) {
+        WUnit<MX> bg, bu;
+        bg.load(w1, w1s, rg, H, u, g);
+        bu.load(w1, w1s, ru, H, u, g);
+        const bf16x8 a = unit_bf16(xr, u, g);
+        ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bg.get(), ag, 0, 0, 0);
+        au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bu.get(), au, 0, 0, 0);
+      }
+    }
+    if (S > 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        red[wave][i][lane] = ag[i];
+        red[wave][4 + i][lane] = au[i];
+      }
+      __syncthreads();
+      if (ks == 0) {
+        for (int sp = 1; sp < S; ++sp) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            ag[i] += red[wave + sp][i][lane];
+            au[i] += red[wave + sp][4 + i][lane];
+          }
+        }
+      }
+      __syncthreads();  // red is rewritten by the next item
+    }
+    if (ks == 0 && active) {
+      const int n = cg * 16 + c;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = g * 4 + i;
+        if (m < nrows) act[(int64_t)(row0 + m) * F + n] = f32_to_bf16_bits(silu_f32(ag[i]) * au[i]);
+      }
+    }
+  }
+}
+
+// GEMM2 for the decode regime: y = W2[e] act over the grouped rows.
+template <bool MX, typename YT>
+__global__ __launch_bounds__(kDecThreads) void ffn2_decode_kernel(
+    const uint16_t* __restrict__ act, int H, int F, int El, const void* __restrict__ w2,
+    const uint8_t* __restrict__ w2s, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    YT* __restrict__ y) {
+  __shared__ float red[kDecWaves][4][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  const bool small = El <= 64;  // uniform
+  TileTab tab{};
+  if (small) tab = load_tile_tab(counts, offsets, El, 16);
+  const int tiles = small ? tab.total : count_tiles(counts, El, 16);
+  const int CG = H / 16, units = F / 32;
+  const int S = decode_split(tiles, CG, units);
+  const int cpb = kDecWaves / S;
+  const int ipt = (CG + cpb - 1) / cpb;
+  const int items = tiles * ipt;
+  const int ks = wave % S, cgl = wave / S;
+  const int per = (units + S - 1) / S;
+  const int u_begin = min(units, ks * per), u_end = min(units, u_begin + per);
+
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int tile = it / ipt, cb = it % ipt;
+    int e = 0, row0 = 0, nrows = 0;
+    if (small) tab_find(tab, 16, tile, e, row0, nrows);
+    else find_tile(counts, offsets, El, 16, tile, e, row0, nrows);
+    const int cg = cb * cpb + cgl;
+    const bool active = cg < CG;
+    f32x4 acc = {0, 0, 0, 0};
+    if (active) {
+      const uint16_t* ar = act + (int64_t)(row0 + (c < nrows ? c : 0)) * F;
+      const int64_t rw = (int64_t)e * H + cg * 16 + c;
+      int u = u_begin;
+      for (; u + kDecUnroll <= u_end; u += kDecUnroll) {
+        WUnit<MX> b[kDecUnroll];
+        bf16x8 a[kDecUnroll];
+#pragma unroll
+        for (int j = 0; j < kDecUnroll; ++j) b[j].load(w2, w2s, rw, F, u + j, g);
+#pragma unroll
+        for (int j = 0; j < kDecUnroll; ++j) a[j] = unit_bf16(ar, u + j, g);
+#pragma unroll
+        for (int j = 0; j < kDecUnroll; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], b[j].get(), acc, 0, 0, 0);
+      }
+      for (; u < u_end; ++u) {
+        WUnit<MX> b;
+        b.load(w2, w2s, rw, F, u, g);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unit_bf16(ar, u, g), b.get(), acc, 0, 0, 0);
+      }
+    }
+    if (S > 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave][i][lane] = acc[i];
+      __syncthreads();
+      if (ks == 0) {
+        for (int sp = 1; sp < S; ++sp) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] += red[wave + sp][i][lane];
+        }
+      }
+      __syncthreads();
+    }
+    if (ks == 0 && active) {
+      const int n = cg * 16 + c;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = g * 4 + i;
+        if (m < nrows) {
+          if constexpr (sizeof(YT) == 2) y[(int64_t)(row0 + m) * H + n] = f32_to_bf16_bits(acc[i]);
+          else y[(int64_t)(row0 + m) * H + n] = acc[i];
+        }
+      }
+    }
+  }
+}
+
+template <bool MX>
+hipError_t launch_decode(const uint16_t* x, int K, int H, int F, int El, const void* w1, const uint8_t* w1s,
+                         const void* w2, const uint8_t* w2s, const int32_t* counts, const int32_t* offsets,
+                         const int32_t* r2s, void* y, int y_dtype, uint16_t* act, hipStream_t stream) {
+  hipLaunchKernelGGL((ffn1_decode_kernel<MX>), dim3(kDecGrid), dim3(kDecThreads), 0, stream, x, K, H, F, El, w1, w1s,
+                     counts, offsets, r2s, act);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (y_dtype == MOE_BF16)
+    hipLaunchKernelGGL((ffn2_decode_kernel<MX, uint16_t>), dim3(kDecGrid), dim3(kDecThreads), 0, stream, act, H, F,
+                       El, w2, w2s, counts, offsets, static_cast<uint16_t*>(y));
+  else
+    hipLaunchKernelGGL((ffn2_decode_kernel<MX, float>), dim3(kDecGrid), dim3(kDecThreads), 0, stream, act, H, F, El,
+                       w2, w2s, counts, offsets, static_cast<float*>(y));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // fp32 weights (small problems): one thread per output element, VALU FMAs.
 
 __device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ offsets, int El, int r) {
@@ -322,13 +632,15 @@ hipError_t dispatch_stream(const uint16_t* x, int64_t N, int K, int H, int F, in
                                            act, stream)
   if (avg >= 48) MOE_FFN_CASE(4);
   if (avg >= 24) MOE_FFN_CASE(2);
-  MOE_FFN_CASE(1);
 #undef MOE_FFN_CASE
+  return launch_decode<MX>(x, K, H, F, El, w1, w1s, w2, w2s, counts, offsets, r2s, y, y_dtype, act, stream);
 }
 
 }  // namespace
 
-size_t grouped_ffn_workspace_bytes(int64_t N, int F, int w_dtype) {
+size_t grouped_ffn_workspace_bytes(int64_t N, int H, int F, int El, int w_dtype) {
+  (void)H;
+  (void)El;
   const size_t elt = (w_dtype == MOE_F32) ? sizeof(float) : sizeof(uint16_t);
   return (size_t)N * (size_t)F * elt;
 }

@@ -69,10 +69,8 @@ int moe_route_compact(const int32_t* topk_ids, int64_t T, int32_t K, const int32
 }
 
 size_t moe_grouped_ffn_workspace_bytes(int64_t T, int32_t K, int32_t H, int32_t F, int32_t E_local, int w_dtype) {
-  (void)H;
-  (void)E_local;
-  if (T <= 0 || K <= 0 || F <= 0) return 0;
-  return moe::grouped_ffn_workspace_bytes(T * K, F, w_dtype);
+  if (T <= 0 || K <= 0 || F <= 0 || H <= 0 || E_local <= 0) return 0;
+  return moe::grouped_ffn_workspace_bytes(T * K, H, F, E_local, w_dtype);
 }
 
 int moe_grouped_ffn(const void* x, int x_dtype, int64_t T, int32_t K, int32_t H, int32_t F, int32_t E_local,
@@ -95,7 +93,7 @@ int moe_grouped_ffn(const void* x, int x_dtype, int64_t T, int32_t K, int32_t H,
     // bf16 rows are read as 16-byte vectors
     if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16)) return MOE_ERR_INVALID_ARG;
   }
-  const size_t need = moe::grouped_ffn_workspace_bytes(T * K, F, w_dtype);
+  const size_t need = moe::grouped_ffn_workspace_bytes(T * K, H, F, E_local, w_dtype);
   if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return MOE_ERR_INVALID_ARG;
   if (!f32_pair && !aligned(y, 16)) return MOE_ERR_INVALID_ARG;  // rows are stored as 16-byte pieces

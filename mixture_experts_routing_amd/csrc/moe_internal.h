@@ -124,7 +124,7 @@ hipError_t launch_route_compact(const int32_t* topk_ids, int64_t N, const int32_
                                 int32_t* slot_to_row, int32_t* row_to_slot, void* workspace,
                                 hipStream_t stream);
 
-size_t grouped_ffn_workspace_bytes(int64_t N, int F, int w_dtype);
+size_t grouped_ffn_workspace_bytes(int64_t N, int H, int F, int El, int w_dtype);
 hipError_t launch_grouped_ffn(const void* x, int x_dtype, int64_t T, int K, int H, int F,
                               int E_local, const void* w1, const uint8_t* w1s, const void* w2,
                               const uint8_t* w2s, int w_dtype, const int32_t* counts,

@@ -15,7 +15,8 @@
 // counts per expert live in LDS.  A per-expert exclusive prefix over the
 // waves (then over blocks) turns group ranks into occurrences.
 //
-//   N <= kSingleMax : one 1024-thread block does everything (decode sizes)
+//   N <= 64         : one wavefront does everything (decode batches)
+//   N <= kSingleMax : one 1024-thread block does everything
 //   larger N        : count kernel (per block counts + in-block ranks, which
 //                     are parked in slot_to_row) -> one-block scan kernel
 //                     (per expert prefix over blocks, offsets) -> scatter
@@ -129,6 +130,51 @@ __device__ __forceinline__ void scan_counts(const int* __restrict__ cnt, int El,
   if (e < El) offs[e] = ex;
   if (e == 0) offs[El] = total;
   __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// one wave: N <= 64 (decode batches).  Every slot sits in one lane; an
+// expert's count is the number of lanes holding its id, read lane by lane.
+
+constexpr int kWaveMax = 64;
+constexpr int kWaveMaxEl = 768;
+
+__global__ __launch_bounds__(64) void compact_wave_kernel(
+    const int32_t* __restrict__ ids, int N, const int32_t* __restrict__ emap, int Eg, int El,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ s2r,
+    int32_t* __restrict__ r2s) {
+  __shared__ int offs[kWaveMaxEl];
+  const int lane = threadIdx.x;
+  const int l = lane < N ? local_of(ids[lane], emap, Eg, El) : -1;
+  int below, total;
+  group_rank(l, lane, below, total);
+  int carry = 0;
+  for (int c0 = 0; c0 < El; c0 += 64) {
+    const int e = c0 + lane;
+    int cnt = 0;
+    for (int j = 0; j < N; ++j) cnt += (__builtin_amdgcn_readlane(l, j) == e) ? 1 : 0;
+    int inc = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(inc, d, 64);
+      if (lane >= d) inc += o;
+    }
+    if (e < El) {
+      const int ex = carry + inc - cnt;
+      counts[e] = cnt;
+      offsets[e] = ex;
+      offs[e] = ex;
+    }
+    carry += __shfl(inc, 63, 64);
+  }
+  if (lane == 0) offsets[El] = carry;
+  __syncthreads();
+  if (lane < N) {
+    const int row = l >= 0 ? offs[l] + below : -1;
+    s2r[lane] = row;
+    if (row >= 0) r2s[row] = lane;
+    if (lane >= carry) r2s[lane] = -1;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -249,6 +295,11 @@ size_t route_compact_workspace_bytes(int64_t N, int E_local) {
 hipError_t launch_route_compact(const int32_t* ids, int64_t N, const int32_t* emap, int Eg, int El,
                                 int32_t* counts, int32_t* offsets, int32_t* s2r, int32_t* r2s,
                                 void* workspace, hipStream_t stream) {
+  if (N <= kWaveMax && El <= kWaveMaxEl) {
+    hipLaunchKernelGGL(compact_wave_kernel, dim3(1), dim3(64), 0, stream, ids, (int)N, emap, Eg, El, counts, offsets,
+                       s2r, r2s);
+    return hipGetLastError();
+  }
   if (N <= kSingleMax) {
     const size_t lds = sizeof(int) * ((size_t)kWaves * El + El + El + 1 + kWaves + 1);
     hipLaunchKernelGGL(compact_single_kernel, dim3(1), dim3(kThreads), lds, stream, ids, (int)N, emap,

@@ -77,7 +77,8 @@ def test_grouped_ffn_validation(lib):
     assert f(*args(1, 2, 4096, 2048)) == 1        # MXFP4 codes without scales
     assert f(*args(1, 1, 4096, 2048, ws=NULL)) == 4
     need = lib.moe_grouped_ffn_workspace_bytes(2, 6, 4096, 2048, 40, 1)
-    assert need == 2 * 6 * 2048 * 2
+    assert need == 2 * 6 * 2048 * 2  # the bf16 act rows
+    assert lib.moe_grouped_ffn_workspace_bytes(4096, 8, 2048, 768, 128, 1) == 4096 * 8 * 768 * 2
     assert f(*args(1, 1, 4096, 2048, wsb=need - 1)) == 4
     mis = ctypes.c_void_p(0x1002)  # bf16 operands must be 16-byte aligned
     a = list(args(1, 1, 4096, 2048))

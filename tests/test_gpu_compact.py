@@ -47,6 +47,12 @@ def test_mxfp4_decode_routes(T, routes):
     (333, 3, 256, 40),
     (1000, 6, 256, 1),       # one local expert
     (3000, 8, 1024, 768),    # widest supported local expert set
+    (8, 8, 128, 128),        # 64 slots: largest one-wavefront size
+    (13, 5, 128, 128),       # 65 slots: smallest one-block size
+    (1, 1, 8, 8),
+    (16, 4, 1024, 768),      # one wavefront, widest local expert set
+    (32, 2, 256, 1),         # one wavefront, one local expert
+    (7, 9, 300, 299),
 ])
 def test_random_routes(N_tokens, K, Eg, El):
     rng = np.random.default_rng(N_tokens + El)
@@ -62,6 +68,8 @@ def test_skewed_and_all_remote():
     # every route on one local expert: 8*5000 rows on one expert
     ids = np.full((5000, 8), 40, np.int32)
     check_compact(ids, emap, El, Eg, "one-hot")
+    # every route on one local expert, one-wavefront size
+    check_compact(np.full((8, 8), 40, np.int32), emap, El, Eg, "one-hot-small")
     # all remote at prefill size
     remote = np.flatnonzero(emap < 0)
     ids = remote[rng.integers(0, remote.size, size=(4096, 8))].astype(np.int32)

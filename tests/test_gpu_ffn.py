@@ -123,6 +123,56 @@ def test_small_shapes_many_tiles_ragged(w_dtype, H, F):
     compare_layer(c, res, ref, "small")
 
 
+def small_case(w_dtype, T, K, Eg, El, H, F, hot, seed, out_dtype="bf16"):
+    rng = np.random.default_rng(seed)
+    emap = synth.random_expert_map(Eg, El, seed=seed)
+    ids = np.stack([rng.choice(Eg, size=K, replace=False) for _ in range(T)]).astype(np.int32)
+    if hot:
+        ids[:, 0] = np.flatnonzero(emap >= 0)[0]
+    w = rng.dirichlet(np.ones(K), size=T).astype(np.float32)
+    x = synth.bf16_normal((T, H), 1.0, seed, 1)
+    if w_dtype == "bf16":
+        w1 = synth.bf16_normal((El, 2 * F, H), 0.05, seed, 2)
+        w2 = synth.bf16_normal((El, H, F), 0.05, seed, 3)
+        w1s = w2s = None
+    else:
+        w1 = rng.integers(0, 256, size=(El, 2 * F, H // 2), dtype=np.uint8)
+        w2 = rng.integers(0, 256, size=(El, H, F // 2), dtype=np.uint8)
+        w1s = rng.integers(119, 128, size=(El, 2 * F, H // 32), dtype=np.uint8)
+        w2s = rng.integers(119, 128, size=(El, H, F // 32), dtype=np.uint8)
+    return synth.MoECase(name=f"small_{w_dtype}_T{T}_{H}_{F}", T=T, E_global=Eg, E_local=El, K=K, H=H, F=F,
+                         renormalize=False, x_dtype="bf16", w_dtype=w_dtype, out_dtype=out_dtype, x=x, w1=w1,
+                         w2=w2, w1_scale=w1s, w2_scale=w2s, topk_ids=ids, topk_weights=w, expert_map=emap)
+
+
+@pytest.mark.parametrize("w_dtype", ["bf16", "mxfp4"])
+@pytest.mark.parametrize("H,F", [(96, 64), (256, 160), (512, 384), (1024, 4096)])
+@pytest.mark.parametrize("T", [1, 3, 9])
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+def test_decode_split_k_shapes(w_dtype, H, F, T, out_dtype):
+    # few rows per expert: the K dimension is split over several blocks and
+    # reduced in a fixed order; K chunks may be uneven or empty
+    c = small_case(w_dtype, T, 4, 12, 6, H, F, hot=(T == 9), seed=H + F + T, out_dtype=out_dtype)
+    res = run_layer(c)
+    ref = oracle.moe_layer(c)
+    compare_layer(c, res, ref, "split")
+    again = run_layer(c)
+    R = int(ref["offsets"][-1])  # rows >= R of y are never written
+    assert torch.equal(again["y"][:R], res["y"][:R]) and torch.equal(again["out"], res["out"])
+
+
+@pytest.mark.parametrize("pattern", ["same", "all_dup", "twelve_local"])
+def test_decode_deterministic(pattern, decode_weights_dev):
+    c = synth.decode_case(pattern, "random", seed=5, with_weights=False)
+    d = case_to_device(c)
+    d["w1"], d["w2"] = decode_weights_dev
+    d["w1_scale"] = d["w2_scale"] = None
+    a = run_layer(c, d)
+    b = run_layer(c, d)
+    R = int(a["offsets"][-1])
+    assert torch.equal(a["y"][:R], b["y"][:R]) and torch.equal(a["out"], b["out"])
+
+
 @pytest.mark.parametrize("ydt,odt", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32"), ("f32", "bf16")])
 @pytest.mark.parametrize("H", [4096, 2048, 136, 7])
 def test_combine(ydt, odt, H):
