@@ -12,8 +12,10 @@ goes to stderr.
 
 Besides the contract fields the line carries:
   roofline      the grouped FFN call (GEMM1 + silu_and_mul kernel and GEMM2
-                kernel), its achieved bf16 MFMA TFLOP/s from HIP events on the
-                launch stream against the 2.5 PFLOP/s dense peak
+                kernel): algorithmic HBM bytes per call over its duration from
+                HIP events on the launch stream, against 8 TB/s (its 256
+                flop/byte lies below the bf16 ridge of ~312, so HBM bounds it);
+                the MFMA rate against the 2.5 PFLOP/s dense peak rides along
   cpu_baseline  the fp64 CPU oracle on a bounded token sample of the same
                 workload, on this host's cores
   breakdown     per-call milliseconds of the step
@@ -52,6 +54,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--quick", action="store_true", help="short secondary runs")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device-to-device copy of MIB MiB five times (the reference kernel "
+                        "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exit")
     return p.parse_args()
 
 
@@ -166,14 +171,22 @@ def bench_prefill(args, dev):
             per[n] += ev[j].elapsed_time(ev[j + 1])
     per = {n: v / args.steps for n, v in per.items()}
     ms_per_step = wall * 1000.0 / args.steps
-    flops = 2.0 * N * (2 * F * H + H * F)  # all routes local: R = T*K
+    # algorithmic work of one moe_grouped_ffn call (all routes local: R = T*K)
+    flops = 2.0 * N * (2 * F * H + H * F)
+    weight_bytes = E * (2 * F * H + H * F) * 2       # every expert's W1 and W2 once
+    row_bytes = N * (2 * F * 2 + H * 2)              # act written + read, y written (bf16)
+    x_bytes = T * H * 2                              # each token's x once
+    alg_bytes = weight_bytes + row_bytes + x_bytes
     ffn_s = per["grouped_ffn"] / 1000.0
-    achieved = flops / ffn_s / 1e12
+    gbs = alg_bytes / ffn_s / 1e9
+    tflops = flops / ffn_s / 1e12
     roofline = {
-        "bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-        "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic_for("grouped_ffn_prefill"),
+        "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_for("grouped_ffn_prefill"),
         "kernel": "moe_grouped_ffn (ffn_tiled_kernel: GEMM1 + silu_and_mul, then GEMM2)",
-        "algorithmic_flops_per_launch": flops, "avg_launch_ms": round(per["grouped_ffn"], 4),
+        "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_ms": round(per["grouped_ffn"], 4),
+        "mfma_tflops": round(tflops, 1), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "algorithmic_flops_per_launch": flops,
     }
     log(f"[bench] prefill layer: {ms_per_step:.3f} ms/step, {T / (ms_per_step / 1e3):.0f} tokens/s; "
         + ", ".join(f"{n} {v:.3f} ms" for n, v in per.items()))
@@ -181,26 +194,22 @@ def bench_prefill(args, dev):
 
 
 def traffic_for(name):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources (else None)."""
+    """HBM bytes per launch from the committed rocprofv3 counter runs
+    (FETCH_SIZE and WRITE_SIZE scaled by a plain-copy calibration), if they
+    were taken on the current kernel sources; else None."""
     p = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
     if not os.path.exists(p):
         return None
     try:
         d = json.load(open(p))
-        if d.get("source_sha256") != kernel_source_hash():
+        h = hashlib.sha256()
+        for f in d["sources"]:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if d.get("source_sha256") != h.hexdigest():
             return None
         return d.get("bytes_per_launch")
     except Exception:
         return None
-
-
-def kernel_source_hash():
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "mixture_experts_routing_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        h.update(open(os.path.join(csrc, f), "rb").read())
-    return h.hexdigest()
 
 
 # ---------------------------------------------------------------------------
@@ -315,8 +324,9 @@ def bench_decode(dev, reps):
 # CPU baseline: the oracle on a bounded sample of the prefill workload
 
 
-def cpu_baseline(c, n_tokens):
-    import numpy as np
+def cpu_baseline(c, n_tokens, min_seconds=10.0, max_reps=20):
+    """The oracle, as it stands, on the first n_tokens tokens of the workload,
+    repeated until at least min_seconds of CPU work have run."""
     from threadpoolctl import threadpool_info
 
     import oracle
@@ -326,13 +336,18 @@ def cpu_baseline(c, n_tokens):
     sub.T = n_tokens
     sub.logits = c.logits[:n_tokens]
     sub.x = c.x[:n_tokens]
-    t0 = time.perf_counter()
-    oracle.moe_layer(sub)
-    dt = time.perf_counter() - t0
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.moe_layer(sub)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or reps >= max_reps:
+            break
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": round(n_tokens / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": round(reps * n_tokens / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {n_tokens} of the {c.T} prefill tokens (gate, compaction, fp64 FFN of all "
-                      f"{n_tokens * c.K} routes over the 128 experts, combine); {dt:.1f} s wall",
+                      f"{n_tokens * c.K} routes over the {c.E_local} experts, combine), run {reps} times; "
+                      f"{dt:.1f} s wall",
             "host_cores_available": len(os.sched_getaffinity(0))}
 
 
@@ -346,6 +361,15 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+        return
     c, ms, per, roofline = bench_prefill(args, dev)
     secondary = {}
     if not args.no_secondary:
@@ -358,7 +382,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
-        cpu = cpu_baseline(c, 1024 if args.quick else c.T)
+        cpu = cpu_baseline(c, 1024 if args.quick else c.T, min_seconds=2.0 if args.quick else 10.0)
         log(f"[bench] cpu: {cpu}")
     line = {
         "metric": "MoE-layer tokens/s + gate Mrows/s; % of HBM BW / MFMA peak, 1 MI355X",
