@@ -50,9 +50,11 @@ typedef enum moe_status {
 typedef enum moe_dtype {
   MOE_F32 = 0,   /* IEEE binary32 */
   MOE_BF16 = 1,  /* bfloat16, round-to-nearest-even on every store */
-  MOE_MXFP4 = 2  /* OCP MX FP4 (E2M1) codes, 2 per byte, element 2i in the low
+  MOE_MXFP4 = 2, /* OCP MX FP4 (E2M1) codes, 2 per byte, element 2i in the low
                     nibble, plus one E8M0 scale byte (2^(e-127)) per 32
                     consecutive elements of the reduction dimension */
+  MOE_BF16_TILED = 3 /* expert weights in bfloat16, stored in the tile-packed
+                        layout written by moe_pack_ffn_weights */
 } moe_dtype;
 
 /*
@@ -123,7 +125,9 @@ size_t moe_route_compact_workspace_bytes(int64_t T, int32_t K, int32_t E_local);
  *                              w2_scale [E_local, H, F/32]
  *   counts, offsets, row_to_slot: as produced by moe_route_compact
  *   y (out)  [T*K, H] (y_dtype MOE_F32 or MOE_BF16); rows >= R are not written
- * Supported (x, w) pairs: (F32, F32), (BF16, BF16), (BF16, MXFP4).
+ * Supported (x, w) pairs: (F32, F32), (BF16, BF16), (BF16, MXFP4),
+ * (BF16, BF16_TILED); BF16_TILED weights come from moe_pack_ffn_weights and
+ * need H % 256 == 0 and F % 128 == 0.
  * The intermediate act is kept in the workspace in bf16 for bf16/MXFP4
  * weights and in fp32 for fp32 weights.  Every sum is taken in a fixed
  * order, so results are deterministic for a given input.
@@ -138,6 +142,31 @@ int moe_grouped_ffn(const void* x, int x_dtype, int64_t T, int32_t K, int32_t H,
                     void* workspace, size_t workspace_bytes, void* stream);
 size_t moe_grouped_ffn_workspace_bytes(int64_t T, int32_t K, int32_t H, int32_t F, int32_t E_local,
                                        int w_dtype);
+
+/*
+ * moe_pack_ffn_weights -- store bf16 expert weights in the tile-packed layout
+ * (MOE_BF16_TILED) that the many-rows-per-expert FFN kernels stream with
+ * contiguous loads.  A one-time transform of the weights (model load), not
+ * part of a layer's pass; the values are unchanged, only their order.
+ * Source of the weights' role: page "Upstream Reference: Deep-Spark xllm +
+ * vllm", section "File Index" (gemm1 / gemm2 of the FusedMoE pipeline); the
+ * layout itself is this library's.
+ *
+ *   w1 [E_local, 2F, H] bf16, w2 [E_local, H, F] bf16 (row-major, as for
+ *   moe_grouped_ffn) -> w1_tiled, w2_tiled: buffers of the same sizes.
+ * Layout: per expert, rows are cut into panels of 256 and the reduction
+ * dimension into chunks of 32 elements; the 256 x 32 block of (panel,
+ * chunk) is stored as 16 KB, chunks of a panel consecutive, panels of an
+ * expert consecutive.  Inside a block, panel row R occupies bytes
+ * [64 R, 64 R + 64), its 16-byte piece p holding elements 8 (p ^ s(R)) .. +8
+ * of the chunk, s(R) = ((R >> 1) ^ (R >> 2)) & 3.  W2 panel nt holds rows
+ * 256 nt + R.  W1 panel nt holds, for R = 64 j + 32 g + r (g = 0 gate, 1 up),
+ * row g F + 128 nt + 32 j + r.
+ * Limits: H % 256 == 0, F % 128 == 0; 16-byte aligned buffers; the outputs
+ * must not overlap the inputs.  MOE_ERR_UNSUPPORTED otherwise.
+ */
+int moe_pack_ffn_weights(const void* w1, const void* w2, int32_t E_local, int32_t H, int32_t F, void* w1_tiled,
+                         void* w2_tiled, void* stream);
 
 /*
  * moe_combine -- top-k weighted combine (direct slot-order gather).

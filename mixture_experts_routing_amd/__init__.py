@@ -13,13 +13,13 @@ from typing import Optional, Tuple
 import torch
 
 from . import _lib
-from ._lib import MOE_BF16, MOE_F32, MOE_MXFP4
+from ._lib import MOE_BF16, MOE_BF16_TILED, MOE_F32, MOE_MXFP4
 
 _LIB = _lib.load()
 
 __all__ = [
     "moe_topk_softmax", "moe_route_compact", "moe_grouped_ffn", "moe_combine", "moe_layer",
-    "MOE_F32", "MOE_BF16", "MOE_MXFP4", "MoeError", "library_path",
+    "MOE_F32", "MOE_BF16", "MOE_MXFP4", "MOE_BF16_TILED", "moe_pack_ffn_weights", "MoeError", "library_path",
 ]
 
 
@@ -126,12 +126,30 @@ def grouped_ffn_workspace_bytes(T: int, K: int, H: int, F: int, E_local: int, w_
     return int(_LIB.moe_grouped_ffn_workspace_bytes(T, K, H, F, E_local, w_dtype))
 
 
+def moe_pack_ffn_weights(w1: torch.Tensor, w2: torch.Tensor, w1_tiled: Optional[torch.Tensor] = None,
+                         w2_tiled: Optional[torch.Tensor] = None, stream=None):
+    """bf16 w1 [E_local, 2F, H], w2 [E_local, H, F] -> the same weights in the
+    tile-packed layout (tensors of the same shapes and dtype, whose memory
+    order is the packed one); pass them to moe_grouped_ffn with tiled=True."""
+    dev = _dev(w1, w2)
+    E_local, H, F = w2.shape
+    if w1_tiled is None:
+        w1_tiled = torch.empty_like(w1)
+    if w2_tiled is None:
+        w2_tiled = torch.empty_like(w2)
+    _check(_LIB.moe_pack_ffn_weights(_ptr(w1), _ptr(w2), E_local, H, F, _ptr(w1_tiled), _ptr(w2_tiled),
+                                     _stream(stream, dev)), "moe_pack_ffn_weights")
+    return w1_tiled, w2_tiled
+
+
 def moe_grouped_ffn(x: torch.Tensor, K: int, w1: torch.Tensor, w2: torch.Tensor, counts: torch.Tensor,
                     offsets: torch.Tensor, row_to_slot: torch.Tensor, w1_scale: Optional[torch.Tensor] = None,
                     w2_scale: Optional[torch.Tensor] = None, y_dtype: Optional[torch.dtype] = None,
-                    y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None):
+                    y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None,
+                    tiled: bool = False):
     """x [T, H]; w1 [E_local, 2F, H] and w2 [E_local, H, F] (f32 / bf16), or
-    uint8 MXFP4 codes [E_local, 2F, H/2], [E_local, H, F/2] with e8m0 scales.
+    uint8 MXFP4 codes [E_local, 2F, H/2], [E_local, H, F/2] with e8m0 scales,
+    or (tiled=True) bf16 weights from moe_pack_ffn_weights.
     Returns y [T*K, H] in the expert-grouped row order (rows >= R unwritten)."""
     dev = _dev(x, w1, w2, counts, offsets, row_to_slot, w1_scale, w2_scale)
     T, H = x.shape
@@ -142,6 +160,10 @@ def moe_grouped_ffn(x: torch.Tensor, K: int, w1: torch.Tensor, w2: torch.Tensor,
     else:
         w_dt = _dt(w1)
         F = w2.shape[2]
+    if tiled:
+        if w_dt != MOE_BF16:
+            raise MoeError("tiled weights must be bfloat16")
+        w_dt = MOE_BF16_TILED
     if y is None:
         y = torch.empty((T * K, H), dtype=y_dtype or x.dtype, device=dev)
     need = grouped_ffn_workspace_bytes(T, K, H, F, E_local, w_dt)
@@ -171,7 +193,7 @@ def moe_layer(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, K: int, logit
               renormalize: bool = False, topk_ids: Optional[torch.Tensor] = None,
               topk_weights: Optional[torch.Tensor] = None, expert_map: Optional[torch.Tensor] = None,
               E_global: Optional[int] = None, w1_scale=None, w2_scale=None, out_dtype=None, y_dtype=None,
-              stream=None) -> dict:
+              stream=None, tiled: bool = False) -> dict:
     """The whole path: gate (if logits are given) -> compaction -> grouped FFN -> combine."""
     tei = None
     if logits is not None:
@@ -179,7 +201,7 @@ def moe_layer(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, K: int, logit
     E_local = w1.shape[0]
     counts, offsets, s2r, r2s = moe_route_compact(topk_ids, expert_map, E_local, E_global=E_global, stream=stream)
     y = moe_grouped_ffn(x, K, w1, w2, counts, offsets, r2s, w1_scale, w2_scale, y_dtype=y_dtype or x.dtype,
-                        stream=stream)
+                        stream=stream, tiled=tiled)
     out = moe_combine(y, topk_weights, s2r, out_dtype=out_dtype or x.dtype, stream=stream)
     return dict(topk_weights=topk_weights, topk_ids=topk_ids, token_expert_indices=tei, counts=counts,
                 offsets=offsets, slot_to_row=s2r, row_to_slot=r2s, y=y, out=out)

@@ -11,7 +11,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libmoe_routing.so")
 HEADER = os.path.join(os.path.dirname(PKG_DIR), "include", "moe_routing.h")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP, MOE_ERR_WORKSPACE = range(5)
-MOE_F32, MOE_BF16, MOE_MXFP4 = range(3)
+MOE_F32, MOE_BF16, MOE_MXFP4, MOE_BF16_TILED = range(4)
 
 _p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -27,6 +27,7 @@ SIGNATURES = {
                                _p, _sz, _p]),
     "moe_grouped_ffn_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32, _int]),
     "moe_combine": (_int, [_p, _int, _p, _p, _i64, _i32, _i32, _p, _int, _p]),
+    "moe_pack_ffn_weights": (_int, [_p, _p, _i32, _i32, _i32, _p, _p, _p]),
     "moe_status_string": (ctypes.c_char_p, [_int]),
     "moe_last_hip_error": (_int, []),
     "moe_version": (ctypes.c_char_p, []),

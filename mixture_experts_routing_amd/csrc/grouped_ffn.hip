@@ -668,9 +668,9 @@ hipError_t launch_grouped_ffn(const void* x, int x_dtype, int64_t T, int K, int 
   }
   uint16_t* act = static_cast<uint16_t*>(workspace);
   const uint16_t* xb = static_cast<const uint16_t*>(x);
-  if (w_dtype == MOE_BF16 && tiled_ffn_applicable(N, H, F, El))
+  if (w_dtype == MOE_BF16_TILED || (w_dtype == MOE_BF16 && tiled_ffn_applicable(N, H, F, El)))
     return launch_tiled_ffn(xb, T, N, K, H, F, El, static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w2),
-                            counts, offsets, r2s, y, y_dtype, act, stream);
+                            w_dtype == MOE_BF16_TILED, counts, offsets, r2s, y, y_dtype, act, stream);
   if (w_dtype == MOE_MXFP4)
     return dispatch_stream<true>(xb, N, K, H, F, El, w1, w1s, w2, w2s, counts, offsets, r2s, y, y_dtype, act, stream);
   return dispatch_stream<false>(xb, N, K, H, F, El, w1, nullptr, w2, nullptr, counts, offsets, r2s, y, y_dtype, act,

@@ -29,10 +29,17 @@
 namespace moe {
 namespace {
 
-constexpr int kTThreads = 256;
-constexpr int kBK = 64;
-constexpr int kLds = kBK + 8;  // bf16 elements per LDS row: 128 B of data + 16 B pad
-constexpr int kBN = 128;
+constexpr int kTThreads = 512;  // 8 waves: 2 per SIMD
+constexpr int kBK = kPanelK;     // K elements per step: 64 bytes of every A and B row
+constexpr int kBN = kPanelRows; // weight rows per block
+constexpr int kStages = 4;      // LDS ring: steps k+1, k+2 in flight while step k computes
+constexpr int kRowBytes = kBK * 2;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14)
+constexpr int wait_vm(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14); }
+constexpr int kWaitLgkm0 = 0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14);
 
 __device__ __forceinline__ bool find_tile_t(const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
                                             int El, int BM, int i, int& e, int& row0, int& nrows) {
@@ -63,108 +70,123 @@ __device__ __forceinline__ bool find_tile_t(const int32_t* __restrict__ counts, 
   return false;
 }
 
-
-// Per-thread global->LDS chunk assignment: chunk i of a tile covers tile row
-// (tid >> 3) + 32 * i and the 16-byte column (tid & 7) of the 128-byte K step.
-template <int MBW>
-struct Stage {
-  u32x4 a[2 * MBW];
-  u32x4 b[4];
-};
-
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   // raw (unstructured) buffer: stride 0, byte-addressed, range-checked
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// The K loop of one block.  LDS holds two K steps (double buffer, one barrier
-// per step); registers hold two more, so the global loads of step k+2 are
-// issued while step k runs on the matrix cores and step k+1 is in flight.
-// Loads are buffer loads: the lane's row offset is a per-lane byte offset
-// fixed for the whole loop, the K position a scalar offset.
-// Wave (wm, wn) owns the 32-row blocks b = 2*mb + wm (interleaved, so both
-// wave rows get the same share of a ragged tile) and 64 weight rows of B.
-// LIVE: blocks of this wave holding valid rows; the others issue no MFMAs.
-template <int MBW, int LIVE>
-__device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t ra_rsrc, const uint32_t (&a_off)[2 * MBW],
-                                      __amdgpu_buffer_rsrc_t rb_rsrc, const uint32_t (&b_off)[4],
-                                      uint16_t (&As)[2][64 * MBW * kLds], uint16_t (&Bs)[2][kBN * kLds],
-                                      f32x16 (&acc)[MBW][2], int K, int nrows, int tid, int lane, int wm, int wn) {
-  constexpr int A_CH = 2 * MBW, B_CH = 4;
-  const int kc = tid & 7;
-  auto gload = [&](Stage<MBW>& st, int k0) {
-    const int sk = k0 * 2;  // bytes
+// LDS layout of one stage: BM A rows then kBN B rows, 64 bytes each (one K
+// step), unpadded.  The four 16-byte pieces of row R are stored XOR-swizzled,
+// piece p at p ^ swz(R): the fragment reads of 8 (or 16) consecutive lanes --
+// consecutive rows, one logical piece -- then hit distinct 16-byte bank groups
+// whether the LDS serves 8 or 16 lanes per cycle.
+__device__ __forceinline__ int swz(int R) { return panel_swz(R); }
+
+// 16-row units of a stage: waves 0-3 move the BM/16 A units (unit u = wave +
+// 4*i), waves 4-7 the kBN/16 = 16 B units, so every load instruction of a
+// wave uses one fixed buffer resource.
+template <int MBW>
+struct Units {
+  static constexpr int BM = 64 * MBW;
+  static constexpr int A = BM / 64;   // A units per A wave
+  static constexpr int B = kBN / 64;  // B units per B wave
+  static constexpr int MAXW = A > B ? A : B;
+};
+
+// The K loop of one block.  Every step each wave moves its units global ->
+// LDS with buffer_load ... lds (no registers): lane l of unit u fills LDS row
+// 16u + l/4, stored piece l%4.  Steps k+1 and k+2 stay in flight while step k
+// runs on the matrix cores; loads past the last step read an empty buffer
+// (all out of range: no memory traffic), so every step issues the same loads
+// and each wave's vmcnt arithmetic holds.
+// Wave (wm, wn) owns the 32-row A blocks b = 2*mb + wm and B rows
+// [64*wn, 64*wn + 64).  LIVE: A blocks of this wave holding valid rows; the
+// others issue no MFMAs.
+template <int MBW, int LIVE, bool PACKED>
+__device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                      __amdgpu_buffer_rsrc_t rz, const uint32_t* __restrict__ src,
+                                      uint8_t* __restrict__ lds, f32x16 (&acc)[MBW][2], int K, int wave, int lane,
+                                      int wm, int wn) {
+  using U = Units<MBW>;
+  constexpr int BM = U::BM;
+  constexpr int STAGE = (BM + kBN) * kRowBytes;
+  const int KT = K / kBK;
+  const bool a_wave = wave < 4;  // uniform
+  auto dma = [&](int slot, int kt) {
+    const bool real = kt < KT;
+    const int sk = real ? kt * kRowBytes : 0;
+    // packed weights: the next K step is the next contiguous block
+    const int skb = real ? kt * (PACKED ? kBN * kRowBytes : kRowBytes) : 0;
+    uint8_t* base = lds + slot * STAGE;
+    if (a_wave) {
+      const __amdgpu_buffer_rsrc_t r = real ? ra : rz;
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) st.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, a_off[i], sk, 0);
+      for (int i = 0; i < U::A; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(base + (wave + 4 * i) * 1024), 16, src[i], sk, 0, 0);
+    } else {
+      const __amdgpu_buffer_rsrc_t r = real ? rb : rz;
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) st.b[i] = __builtin_amdgcn_raw_buffer_load_b128(rb_rsrc, b_off[i], sk, 0);
-  };
-  auto lstore = [&](const Stage<MBW>& st, int buf) {
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i)
-      *reinterpret_cast<u32x4*>(&As[buf][((tid >> 3) + 32 * i) * kLds + kc * 8]) = st.a[i];
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i)
-      *reinterpret_cast<u32x4*>(&Bs[buf][((tid >> 3) + 32 * i) * kLds + kc * 8]) = st.b[i];
-  };
-  auto compute = [&](int buf) {
-    const uint16_t* as = &As[buf][(wm * 32 + (lane & 31)) * kLds + (lane >> 5) * 8];
-    const uint16_t* bs = &Bs[buf][(wn * 64 + (lane & 31)) * kLds + (lane >> 5) * 8];
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(bs + ks * 16);
-      const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(bs + 32 * kLds + ks * 16);
-      bf16x8 a[LIVE > 0 ? LIVE : 1];
-#pragma unroll
-      for (int mb = 0; mb < LIVE; ++mb) a[mb] = *reinterpret_cast<const bf16x8*>(as + mb * 64 * kLds + ks * 16);
-#pragma unroll
-      for (int mb = 0; mb < LIVE; ++mb) {
-        acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b0, acc[mb][0], 0, 0, 0);
-        acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b1, acc[mb][1], 0, 0, 0);
-      }
+      for (int i = 0; i < U::B; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(base + BM * kRowBytes + (wave - 4 + 4 * i) * 1024), 16,
+                                                 src[i], skb, 0, 0);
     }
   };
-  const int KT = K / kBK;
-  Stage<MBW> s0, s1;
-  // Every load in the steady state is unconditional so that the compiler's
-  // vmcnt waits before each LDS store release only the older stage: step k+2
-  // stays in flight while step k computes.  (A load count that differs
-  // between control paths makes the wait pass fall back to waiting for the
-  // newest loads too.)
-  gload(s0, 0);
-  gload(s1, (KT > 1 ? 1 : 0) * kBK);
-  lstore(s0, 0);
-  __syncthreads();
-  // top of each pair: LDS[0] holds step kt, s1 holds step kt+1 (in flight)
-  int kt = 0;
-  for (; kt + 3 < KT; kt += 2) {
-    gload(s0, (kt + 2) * kBK);
-    compute(0);
-    lstore(s1, 1);
-    __syncthreads();
-    gload(s1, (kt + 3) * kBK);
-    compute(1);
-    lstore(s0, 0);
-    __syncthreads();
+  // fragment addresses (bytes within a stage): lane l reads row R, logical
+  // piece 2*ks + l/32
+  const int r32 = lane & 31, hi = lane >> 5, sw = swz(r32);
+  int a_addr[LIVE > 0 ? LIVE : 1][2], b_addr[2][2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+    for (int mb = 0; mb < LIVE; ++mb) a_addr[mb][ks] = ((2 * mb + wm) * 32 + r32) * kRowBytes + (((2 * ks + hi) ^ sw) * 16);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      b_addr[nb][ks] = (BM + wn * 64 + nb * 32 + r32) * kRowBytes + (((2 * ks + hi) ^ sw) * 16);
   }
-  const int left = KT - kt;  // 1, 2 or 3 steps
-  if (left == 3) {
-    gload(s0, (kt + 2) * kBK);
-    compute(0);
-    lstore(s1, 1);
-    __syncthreads();
-    compute(1);
-    lstore(s0, 0);
-    __syncthreads();
-    compute(0);
-  } else if (left == 2) {
-    compute(0);
-    lstore(s1, 1);
-    __syncthreads();
-    compute(1);
-  } else {
-    compute(0);
+  // All fragments of the step are requested before the first MFMA (the
+  // sched_barrier keeps the compiler from sinking the reads next to their
+  // uses), so the reads of the second K half arrive while the first half runs
+  // on the matrix core.
+  auto compute = [&](int slot) {
+    const uint8_t* base = lds + slot * STAGE;
+    bf16x8 a[2][LIVE > 0 ? LIVE : 1], b[2][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) b[ks][nb] = *reinterpret_cast<const bf16x8*>(base + b_addr[nb][ks]);
+#pragma unroll
+      for (int mb = 0; mb < LIVE; ++mb) a[ks][mb] = *reinterpret_cast<const bf16x8*>(base + a_addr[mb][ks]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < LIVE; ++mb) {
+        acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][mb], b[ks][0], acc[mb][0], 0, 0, 0);
+        acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][mb], b[ks][1], acc[mb][1], 0, 0, 0);
+      }
+  };
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s) dma(s, s);
+  int slot = 0;
+  for (int kt = 0; kt < KT; ++kt) {
+    // own loads of step kt have landed once only the kStages-2 newer steps remain
+    if (a_wave) __builtin_amdgcn_s_waitcnt(wait_vm((kStages - 2) * U::A));
+    else __builtin_amdgcn_s_waitcnt(wait_vm((kStages - 2) * U::B));
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // the slot read in step kt-1 is free: every wave has passed the barrier
+    const int fill = slot == 0 ? kStages - 1 : slot - 1;
+    dma(fill, kt + kStages - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(slot);
+    slot = slot == kStages - 1 ? 0 : slot + 1;
   }
+  // drain the trailing (empty) loads before LDS is reused
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
 }
 
 // Block -> (M-tile, N-tile).  Workgroups are dispatched to the 8 XCDs round
@@ -183,55 +205,63 @@ __device__ __forceinline__ void xcd_map(int L, int NT, int& mt, int& nt) {
 //                topk, W = W1 [El, 2*Fh, K], out = act [N, Fh] (bf16 bits).
 // GATED = false: GEMM2.  A = act [N, K] (grouped rows), W = W2 [El, Nw, K],
 //                out = y [N, Nw] (OT = bf16 bits or float).
-template <int MBW, bool GATED, typename OT>
+// PACKED: W is in the tile-packed layout (one contiguous 16 KB block per K
+// step of the block's panel), else row-major.
+template <int MBW, bool GATED, bool PACKED, typename OT>
 __global__ __launch_bounds__(kTThreads) void ffn_tiled_kernel(
     const uint16_t* __restrict__ A, int K, int topk, const int32_t* __restrict__ r2s, const uint16_t* __restrict__ W,
     int Nw, int Fh, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, int El,
     OT* __restrict__ out, int ldo, uint32_t a_bytes, int NT) {
-  constexpr int BM = 64 * MBW;
-  constexpr int A_CH = BM * 8 / kTThreads;   // 16-byte chunks of the A tile per thread
-  constexpr int B_CH = kBN * 8 / kTThreads;  // ... of the B tile
-  static_assert(A_CH == 2 * MBW && B_CH == 4, "thread/chunk mapping");
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kLds];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kBN * kLds];
+  using U = Units<MBW>;
+  constexpr int BM = U::BM;
+  constexpr int RING = kStages * (BM + kBN) * kRowBytes;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[RING];
 
   int mt, ntile;
   xcd_map(blockIdx.x, NT, mt, ntile);
   int e, row0, nrows;
   if (!find_tile_t(counts, offsets, El, BM, mt, e, row0, nrows)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int n0 = ntile * (GATED ? kBN / 2 : kBN);  // first act column (GEMM1) / output column (GEMM2)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: resource choices stay scalar
+  const int wm = wave >> 2, wn = wave & 3;
+  constexpr int OC = GATED ? kBN / 2 : kBN;  // output columns of the block
+  const int n0 = ntile * OC;                 // first act column (GEMM1) / output column (GEMM2)
 
-  // A: byte offsets of this thread's rows.  Rows past nrows get an offset
-  // beyond the buffer's range (a_bytes < 2^31 and K offsets stay below 2^31):
-  // the range-checked buffer load returns zeros for them without a memory
-  // access, so every load is unconditional and the compiler can keep exact
-  // vmcnt waits (two K steps in flight).
-  const int kc = tid & 7;
-  const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(A, a_bytes);
-  uint32_t a_off[A_CH];
-#pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int r = (tid >> 3) + 32 * i;
-    if (r < nrows) {
-      const uint32_t row = GATED ? (uint32_t)(r2s[row0 + r] / topk) : (uint32_t)(row0 + r);
-      a_off[i] = (row * (uint32_t)K + kc * 8) * 2u;
-    } else {
-      a_off[i] = 0x80000000u;
-    }
-  }
-  // B: this expert's weight rows, offsets relative to the expert's slab
+  // Source byte offsets of this lane's DMA rows (fixed for the whole loop;
+  // the K position is the scalar offset).  A rows past nrows get an offset
+  // beyond the buffer's range (a_bytes < 2^31, K offsets < 2^31): the
+  // range-checked load reads nothing for them.
   const int rows_e = GATED ? 2 * Fh : Nw;
-  const __amdgpu_buffer_rsrc_t rb_rsrc = make_rsrc(W + (int64_t)e * rows_e * K, (uint32_t)rows_e * K * 2u);
-  uint32_t b_off[B_CH];
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, a_bytes);
+  const __amdgpu_buffer_rsrc_t rb =
+      PACKED ? make_rsrc(W + ((int64_t)e * rows_e + (int64_t)ntile * kBN) * K, (uint32_t)kBN * K * 2u)
+             : make_rsrc(W + (int64_t)e * rows_e * K, (uint32_t)rows_e * K * 2u);
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(A, 0u);
+  uint32_t src[U::MAXW];
 #pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int c = (tid >> 3) + 32 * i;
-    uint32_t wrow;
-    if constexpr (GATED) wrow = (((c >> 5) & 1) ? Fh : 0) + n0 + (c >> 6) * 32 + (c & 31);
-    else wrow = n0 + c;
-    b_off[i] = (wrow * (uint32_t)K + kc * 8) * 2u;
+  for (int i = 0; i < U::MAXW; ++i) {
+    if (wave < 4) {
+      const int R = (wave + 4 * i) * 16 + (lane >> 2);  // A row of the tile
+      const uint32_t piece = (uint32_t)((lane & 3) ^ swz(R)) * 16u;
+      if (i < U::A && R < nrows) {
+        const uint32_t row = GATED ? (uint32_t)(r2s[row0 + R] / topk) : (uint32_t)(row0 + R);
+        src[i] = row * (uint32_t)K * 2u + piece;
+      } else {
+        src[i] = 0x80000000u;
+      }
+    } else {
+      const int c = (wave - 4 + 4 * i) * 16 + (lane >> 2);  // B row of the tile
+      uint32_t off;
+      if constexpr (PACKED) {
+        // a packed K-step block is the LDS image: unit u at u KB, lane at 16 B
+        off = (uint32_t)((wave - 4 + 4 * i) * 1024 + lane * 16);
+      } else {
+        const uint32_t piece = (uint32_t)((lane & 3) ^ swz(BM + c)) * 16u;
+        const uint32_t wrow = GATED ? (uint32_t)panel_w1_row(c, ntile, Fh) : (uint32_t)panel_w2_row(c, ntile);
+        off = wrow * (uint32_t)K * 2u + piece;
+      }
+      src[i] = i < U::B ? off : 0x80000000u;
+    }
   }
 
   f32x16 acc[MBW][2];
@@ -247,45 +277,54 @@ __global__ __launch_bounds__(kTThreads) void ffn_tiled_kernel(
   live = live < 0 ? 0 : (live > MBW ? MBW : live);
 
   switch (live) {
-    case 0: kloop<MBW, 0>(ra_rsrc, a_off, rb_rsrc, b_off, As, Bs, acc, K, nrows, tid, lane, wm, wn); break;
-    case 1: kloop<MBW, 1>(ra_rsrc, a_off, rb_rsrc, b_off, As, Bs, acc, K, nrows, tid, lane, wm, wn); break;
-    case 2: kloop<MBW, (MBW >= 2 ? 2 : MBW)>(ra_rsrc, a_off, rb_rsrc, b_off, As, Bs, acc, K, nrows, tid, lane, wm, wn); break;
-    case 3: kloop<MBW, (MBW >= 3 ? 3 : MBW)>(ra_rsrc, a_off, rb_rsrc, b_off, As, Bs, acc, K, nrows, tid, lane, wm, wn); break;
-    case 4: kloop<MBW, (MBW >= 4 ? 4 : MBW)>(ra_rsrc, a_off, rb_rsrc, b_off, As, Bs, acc, K, nrows, tid, lane, wm, wn); break;
-    default: kloop<MBW, MBW>(ra_rsrc, a_off, rb_rsrc, b_off, As, Bs, acc, K, nrows, tid, lane, wm, wn); break;
+    case 0: kloop<MBW, 0, PACKED>(ra, rb, rz, src, lds, acc, K, wave, lane, wm, wn); break;
+    case 1: kloop<MBW, 1, PACKED>(ra, rb, rz, src, lds, acc, K, wave, lane, wm, wn); break;
+    case 2: kloop<MBW, (MBW >= 2 ? 2 : MBW), PACKED>(ra, rb, rz, src, lds, acc, K, wave, lane, wm, wn); break;
+    case 3: kloop<MBW, (MBW >= 3 ? 3 : MBW), PACKED>(ra, rb, rz, src, lds, acc, K, wave, lane, wm, wn); break;
+    case 4: kloop<MBW, (MBW >= 4 ? 4 : MBW), PACKED>(ra, rb, rz, src, lds, acc, K, wave, lane, wm, wn); break;
+    default: kloop<MBW, MBW, PACKED>(ra, rb, rz, src, lds, acc, K, wave, lane, wm, wn); break;
   }
 
   // Epilogue.  acc[mb][nb][j] is C[row (j/4)*8 + (lane/32)*4 + j%4][col lane%32]
   // of block b = 2*mb + wm.  bf16 results are staged through LDS (the K loop
-  // is done with it) so that global stores are whole 16-byte row pieces.
+  // is done with it) so that global stores are whole 16-byte row pieces; the
+  // A blocks of the two wave rows go in two passes (b even, then b odd).
   const int cl = lane & 31;
   if constexpr (GATED || sizeof(OT) == 2) {
-    constexpr int OC = GATED ? kBN / 2 : kBN;  // output columns of the block
-    constexpr int OS = OC + 8;                 // padded LDS row (bf16 elements)
-    static_assert(BM * OS <= 2 * BM * kLds, "staging tile fits in the A buffers");
-    uint16_t* st = &As[0][0];
-#pragma unroll
-    for (int mb = 0; mb < MBW; ++mb) {
-      if (mb >= live) continue;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int r = (2 * mb + wm) * 32 + (j >> 2) * 8 + (lane >> 5) * 4 + (j & 3);
-        if constexpr (GATED) {
-          const float g = acc[mb][0][j], u = acc[mb][1][j];
-          st[r * OS + wn * 32 + cl] = f32_to_bf16_bits(g / (1.0f + expf(-g)) * u);
-        } else {
-          st[r * OS + wn * 64 + cl] = f32_to_bf16_bits(acc[mb][0][j]);
-          st[r * OS + wn * 64 + 32 + cl] = f32_to_bf16_bits(acc[mb][1][j]);
-        }
-      }
-    }
-    __syncthreads();
+    constexpr int OS = OC + 8;  // padded LDS row (bf16 elements)
+    static_assert(MBW * 32 * OS * 2 <= RING, "staging tile fits in the LDS ring");
+    uint16_t* st = reinterpret_cast<uint16_t*>(lds);
     constexpr int CPR = OC / 8;  // 16-byte pieces per row
     uint16_t* ob = reinterpret_cast<uint16_t*>(out);
-    for (int p = tid; p < nrows * CPR; p += kTThreads) {
-      const int r = p / CPR, c8 = (p % CPR) * 8;
-      *reinterpret_cast<u32x4*>(ob + (int64_t)(row0 + r) * ldo + n0 + c8) =
-          *reinterpret_cast<const u32x4*>(st + r * OS + c8);
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      if (wm == pass) {
+#pragma unroll
+        for (int mb = 0; mb < MBW; ++mb) {
+          if (mb >= live) continue;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int r = mb * 32 + (j >> 2) * 8 + (lane >> 5) * 4 + (j & 3);  // row within this pass
+            if constexpr (GATED) {
+              const float g = acc[mb][0][j], u = acc[mb][1][j];
+              st[r * OS + wn * 32 + cl] = f32_to_bf16_bits(g / (1.0f + expf(-g)) * u);
+            } else {
+              st[r * OS + wn * 64 + cl] = f32_to_bf16_bits(acc[mb][0][j]);
+              st[r * OS + wn * 64 + 32 + cl] = f32_to_bf16_bits(acc[mb][1][j]);
+            }
+          }
+        }
+      }
+      __syncthreads();
+      // pass rows: blocks b = 2*mb + pass, b*32 < nrows
+      for (int p = tid; p < MBW * 32 * CPR; p += kTThreads) {
+        const int r = p / CPR, c8 = (p % CPR) * 8;
+        const int tr = (2 * (r >> 5) + pass) * 32 + (r & 31);  // row of the tile
+        if (tr < nrows)
+          *reinterpret_cast<u32x4*>(ob + (int64_t)(row0 + tr) * ldo + n0 + c8) =
+              *reinterpret_cast<const u32x4*>(st + r * OS + c8);
+      }
+      __syncthreads();
     }
   } else {
 #pragma unroll
@@ -302,47 +341,93 @@ __global__ __launch_bounds__(kTThreads) void ffn_tiled_kernel(
   }
 }
 
-template <int MBW>
+template <int MBW, bool PACKED>
 hipError_t launch_tiled_mbw(const uint16_t* x, int64_t T, int64_t N, int topk, int H, int F, int El,
                             const uint16_t* w1, const uint16_t* w2, const int32_t* counts, const int32_t* offsets,
                             const int32_t* r2s, void* y, int y_dtype, uint16_t* act, hipStream_t stream) {
   constexpr int BM = 64 * MBW;
   int64_t mtiles = (N + BM - 1) / BM + (N < El ? N : (int64_t)El);
   mtiles = (mtiles + 7) / 8 * 8;  // whole rounds of the 8 XCDs
-  const int nt1 = F / (kBN / 2), nt2 = H / kBN;
-  hipLaunchKernelGGL((ffn_tiled_kernel<MBW, true, uint16_t>), dim3((unsigned)(mtiles * nt1)), dim3(kTThreads), 0,
-                     stream, x, H, topk, r2s, w1, 2 * F, F, counts, offsets, El, act, F, (uint32_t)(T * H * 2), nt1);
+  const int nt1 = F / (kBN / 2), nt2 = H / kBN;  // 128 act columns / 256 output columns per block
+  hipLaunchKernelGGL((ffn_tiled_kernel<MBW, true, PACKED, uint16_t>), dim3((unsigned)(mtiles * nt1)), dim3(kTThreads),
+                     0, stream, x, H, topk, r2s, w1, 2 * F, F, counts, offsets, El, act, F, (uint32_t)(T * H * 2), nt1);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const dim3 g2((unsigned)(mtiles * nt2));
   const uint32_t act_bytes = (uint32_t)(N * F * 2);
   if (y_dtype == MOE_BF16)
-    hipLaunchKernelGGL((ffn_tiled_kernel<MBW, false, uint16_t>), g2, dim3(kTThreads), 0, stream, act, F, topk, r2s,
-                       w2, H, F, counts, offsets, El, static_cast<uint16_t*>(y), H, act_bytes, nt2);
+    hipLaunchKernelGGL((ffn_tiled_kernel<MBW, false, PACKED, uint16_t>), g2, dim3(kTThreads), 0, stream, act, F, topk,
+                       r2s, w2, H, F, counts, offsets, El, static_cast<uint16_t*>(y), H, act_bytes, nt2);
   else
-    hipLaunchKernelGGL((ffn_tiled_kernel<MBW, false, float>), g2, dim3(kTThreads), 0, stream, act, F, topk, r2s, w2,
-                       H, F, counts, offsets, El, static_cast<float*>(y), H, act_bytes, nt2);
+    hipLaunchKernelGGL((ffn_tiled_kernel<MBW, false, PACKED, float>), g2, dim3(kTThreads), 0, stream, act, F, topk, r2s,
+                       w2, H, F, counts, offsets, El, static_cast<float*>(y), H, act_bytes, nt2);
   return hipGetLastError();
 }
 
 }  // namespace
 
+bool tiled_shape_ok(int64_t N, int H, int F) {
+  // 128 act columns per GEMM1 block, 256 output columns per GEMM2 block (so
+  // both reduction lengths are multiples of the 32-wide step).  Buffer
+  // offsets are 32-bit byte offsets: x and act must stay below 2 GiB (offsets
+  // from 2^31 up mark padding rows), one expert's weights below 4 GiB.
+  return (H % kBN == 0) && (F % (kBN / 2) == 0) && (N * (int64_t)(H > F ? H : F) * 2 < ((int64_t)1 << 31)) &&
+         ((int64_t)2 * F * H * 2 < ((int64_t)1 << 32));
+}
+
 bool tiled_ffn_applicable(int64_t N, int H, int F, int El) {
-  // K steps of 64 for both GEMMs, 64 act columns per GEMM1 block, 128 output
-  // columns per GEMM2 block, and enough rows per expert to fill the tiles
-  // buffer offsets are 32-bit byte offsets: x and act must stay below 2 GiB
-  // (offsets from 2^31 up mark padding rows), one expert's weights below 4 GiB
-  return (H % kBN == 0) && (F % 64 == 0) && (N / (El > 0 ? El : 1) >= 96) &&
-         (N * (int64_t)(H > F ? H : F) * 2 < ((int64_t)1 << 31)) && ((int64_t)2 * F * H * 2 < ((int64_t)1 << 32));
+  // row-major weights: worth it once experts hold enough rows to fill the tiles
+  return tiled_shape_ok(N, H, F) && (N / (El > 0 ? El : 1) >= 96);
 }
 
 hipError_t launch_tiled_ffn(const uint16_t* x, int64_t T, int64_t N, int topk, int H, int F, int El,
-                            const uint16_t* w1, const uint16_t* w2, const int32_t* counts, const int32_t* offsets,
-                            const int32_t* r2s, void* y, int y_dtype, uint16_t* act, hipStream_t stream) {
-  const int64_t avg = N / El;
-  if (avg >= 192)
-    return launch_tiled_mbw<5>(x, T, N, topk, H, F, El, w1, w2, counts, offsets, r2s, y, y_dtype, act, stream);
-  return launch_tiled_mbw<2>(x, T, N, topk, H, F, El, w1, w2, counts, offsets, r2s, y, y_dtype, act, stream);
+                            const uint16_t* w1, const uint16_t* w2, bool packed, const int32_t* counts,
+                            const int32_t* offsets, const int32_t* r2s, void* y, int y_dtype, uint16_t* act,
+                            hipStream_t stream) {
+  const bool big = N / El >= 192;
+  if (packed)
+    return big ? launch_tiled_mbw<5, true>(x, T, N, topk, H, F, El, w1, w2, counts, offsets, r2s, y, y_dtype, act, stream)
+               : launch_tiled_mbw<2, true>(x, T, N, topk, H, F, El, w1, w2, counts, offsets, r2s, y, y_dtype, act, stream);
+  return big ? launch_tiled_mbw<5, false>(x, T, N, topk, H, F, El, w1, w2, counts, offsets, r2s, y, y_dtype, act, stream)
+             : launch_tiled_mbw<2, false>(x, T, N, topk, H, F, El, w1, w2, counts, offsets, r2s, y, y_dtype, act, stream);
+}
+
+// ---------------------------------------------------------------------------
+// moe_pack_ffn_weights: row-major bf16 W1 / W2 -> tile-packed layout.  One
+// thread per 16-byte piece of the destination (contiguous stores).
+
+namespace {
+
+__global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ w, uint16_t* __restrict__ wt,
+                                                   int64_t pieces, int rows, int K, int gated, int F) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= pieces) return;
+  const int64_t per_expert = (int64_t)rows * K / 8;
+  const int64_t e = q / per_expert;
+  int64_t r = q - e * per_expert;
+  const int64_t per_panel = (int64_t)kPanelRows * K / 8;
+  const int nt = (int)(r / per_panel);
+  r -= (int64_t)nt * per_panel;
+  const int kt = (int)(r / (kPanelRows * 4));
+  const int rem = (int)(r - (int64_t)kt * kPanelRows * 4);
+  const int R = rem >> 2, p = rem & 3;
+  const int row = gated ? panel_w1_row(R, nt, F) : panel_w2_row(R, nt);
+  const int k = kt * kPanelK + ((p ^ panel_swz(R)) * 8);
+  const u32x4 v = *reinterpret_cast<const u32x4*>(w + ((int64_t)e * rows + row) * K + k);
+  *reinterpret_cast<u32x4*>(wt + q * 8) = v;
+}
+
+}  // namespace
+
+hipError_t launch_pack_ffn_weights(const uint16_t* w1, const uint16_t* w2, int El, int H, int F, uint16_t* w1t,
+                                   uint16_t* w2t, hipStream_t stream) {
+  const int64_t p1 = (int64_t)El * 2 * F * H / 8, p2 = (int64_t)El * H * F / 8;
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)((p1 + 255) / 256)), dim3(256), 0, stream, w1, w1t, p1, 2 * F, H, 1,
+                     F);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)((p2 + 255) / 256)), dim3(256), 0, stream, w2, w2t, p2, H, F, 0, F);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -82,7 +82,9 @@ int moe_grouped_ffn(const void* x, int x_dtype, int64_t T, int32_t K, int32_t H,
   const bool f32_pair = (x_dtype == MOE_F32 && w_dtype == MOE_F32);
   const bool bf16_pair = (x_dtype == MOE_BF16 && w_dtype == MOE_BF16);
   const bool mx_pair = (x_dtype == MOE_BF16 && w_dtype == MOE_MXFP4);
-  if (!f32_pair && !bf16_pair && !mx_pair) return MOE_ERR_UNSUPPORTED;
+  const bool tiled_pair = (x_dtype == MOE_BF16 && w_dtype == MOE_BF16_TILED);
+  if (!f32_pair && !bf16_pair && !mx_pair && !tiled_pair) return MOE_ERR_UNSUPPORTED;
+  if (tiled_pair && !moe::tiled_shape_ok(T * (int64_t)K, H, F)) return MOE_ERR_UNSUPPORTED;
   if (!f32_pair && (H % 32 != 0 || F % 32 != 0)) return MOE_ERR_UNSUPPORTED;
   if (T * (int64_t)K >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
   if (f32_pair && T * (int64_t)K * (int64_t)(H > F ? H : F) >= ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
@@ -100,6 +102,26 @@ int moe_grouped_ffn(const void* x, int x_dtype, int64_t T, int32_t K, int32_t H,
   return hip_status(moe::launch_grouped_ffn(x, x_dtype, T, K, H, F, E_local, w1, w1_scale, w2, w2_scale, w_dtype,
                                             counts, offsets, row_to_slot, y, y_dtype, workspace,
                                             static_cast<hipStream_t>(stream)));
+}
+
+int moe_pack_ffn_weights(const void* w1, const void* w2, int32_t E_local, int32_t H, int32_t F, void* w1_tiled,
+                         void* w2_tiled, void* stream) {
+  if (E_local < 1 || H < 1 || F < 1) return MOE_ERR_INVALID_ARG;
+  if (H % moe::kPanelRows != 0 || F % (moe::kPanelRows / 2) != 0) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)2 * F * H * 2 >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+  if (!w1 || !w2 || !w1_tiled || !w2_tiled) return MOE_ERR_INVALID_ARG;
+  if (!aligned(w1, 16) || !aligned(w2, 16) || !aligned(w1_tiled, 16) || !aligned(w2_tiled, 16))
+    return MOE_ERR_INVALID_ARG;
+  const uintptr_t b1 = (uintptr_t)E_local * 2 * F * H * 2, b2 = (uintptr_t)E_local * H * F * 2;
+  auto overlap = [](const void* a, uintptr_t na, const void* b, uintptr_t nb) {
+    return (uintptr_t)a < (uintptr_t)b + nb && (uintptr_t)b < (uintptr_t)a + na;
+  };
+  if (overlap(w1_tiled, b1, w1, b1) || overlap(w1_tiled, b1, w2, b2) || overlap(w2_tiled, b2, w1, b1) ||
+      overlap(w2_tiled, b2, w2, b2) || overlap(w1_tiled, b1, w2_tiled, b2))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_pack_ffn_weights(static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w2),
+                                                 E_local, H, F, static_cast<uint16_t*>(w1_tiled),
+                                                 static_cast<uint16_t*>(w2_tiled), static_cast<hipStream_t>(stream)));
 }
 
 int moe_combine(const void* y, int y_dtype, const float* topk_weights, const int32_t* slot_to_row, int64_t T,

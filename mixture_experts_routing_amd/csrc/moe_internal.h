@@ -131,11 +131,35 @@ hipError_t launch_grouped_ffn(const void* x, int x_dtype, int64_t T, int K, int 
                               const int32_t* offsets, const int32_t* row_to_slot, void* y,
                               int y_dtype, void* workspace, hipStream_t stream);
 
-// LDS-tiled MFMA path for many rows per expert (bf16 weights)
+// Tile-packed bf16 weight layout (MOE_BF16_TILED), written by
+// moe_pack_ffn_weights and read by the tiled FFN kernels.  Per expert, the
+// weight rows are cut into panels of kPanelRows rows and the reduction
+// dimension into chunks of kPanelK elements; chunk (panel, kt) is stored as
+// one contiguous 16 KB block, kt fastest after the panel, holding panel row R
+// (64 bytes) at R*64 with its four 16-byte pieces XOR-swizzled: stored piece
+// p holds elements kt*32 + 8*(p ^ panel_swz(R)) .. +8.  The block is the
+// byte image of the kernels' LDS stage, so it moves with contiguous loads.
+// GEMM1 panels interleave 32 gate rows and the matching 32 up rows.
+constexpr int kPanelRows = 256;
+constexpr int kPanelK = 32;
+__host__ __device__ constexpr int panel_swz(int R) { return ((R >> 1) ^ (R >> 2)) & 3; }
+// W1 row held by row R of GEMM1 panel nt (gate rows [0,F), up rows [F,2F))
+__host__ __device__ constexpr int panel_w1_row(int R, int nt, int F) {
+  return (((R >> 5) & 1) ? F : 0) + nt * (kPanelRows / 2) + (R >> 6) * 32 + (R & 31);
+}
+// W2 row held by row R of GEMM2 panel nt
+__host__ __device__ constexpr int panel_w2_row(int R, int nt) { return nt * kPanelRows + R; }
+
+// LDS-tiled MFMA path for many rows per expert (bf16 weights, row-major or
+// tile-packed)
 bool tiled_ffn_applicable(int64_t N, int H, int F, int El);
+bool tiled_shape_ok(int64_t N, int H, int F);
 hipError_t launch_tiled_ffn(const uint16_t* x, int64_t T, int64_t N, int topk, int H, int F, int El,
-                            const uint16_t* w1, const uint16_t* w2, const int32_t* counts, const int32_t* offsets,
-                            const int32_t* r2s, void* y, int y_dtype, uint16_t* act, hipStream_t stream);
+                            const uint16_t* w1, const uint16_t* w2, bool packed, const int32_t* counts,
+                            const int32_t* offsets, const int32_t* r2s, void* y, int y_dtype, uint16_t* act,
+                            hipStream_t stream);
+hipError_t launch_pack_ffn_weights(const uint16_t* w1, const uint16_t* w2, int El, int H, int F, uint16_t* w1t,
+                                   uint16_t* w2t, hipStream_t stream);
 
 hipError_t launch_combine(const void* y, int y_dtype, const float* w, const int32_t* slot_to_row,
                           int64_t T, int K, int H, void* out, int out_dtype, hipStream_t stream);
