@@ -4,21 +4,31 @@
 // expand -> gemm1 -> silu_and_mul -> gemm2 order of the FusedMoE pipeline on
 // the "Upstream Reference: Deep-Spark xllm + vllm" page, "File Index"; the
 // expert-grouped layout and cross-row weight reuse of the b70 lab note "MTP1
-// M2 compact scheduler closure", design paragraph), tiled for MFMA
-// throughput instead of pure weight streaming:
+// M2 compact scheduler closure", design paragraph), tiled for the matrix
+// cores:
 //
-//   block tile   BM rows of one expert x 128 weight rows, K step 64, 4 waves
-//                in a 2 x 2 grid; each wave owns (BM/2) x 64 and issues
-//                v_mfma_f32_32x32x16_bf16 on (BM/64) x 2 accumulator tiles
-//   LDS          double-buffered A and B tiles, rows padded by 16 bytes so the
-//                16-byte fragment reads of 8 consecutive lanes hit distinct
-//                banks; one barrier per K step; global loads of step k+1 are
-//                in flight while step k runs on the matrix cores
-//   GEMM1        A rows are gathered from x through row_to_slot (expand), the
-//                128 weight rows are 64 gate rows and the matching 64 up rows
-//                interleaved in 32-row groups, so each lane holds a gate value
-//                and its up value and silu(g)*u is formed in registers
-//   GEMM2        A rows are act rows; 128 output columns per block
+//   tile         BM (320 or 128) rows of one expert x 256 weight rows; K is
+//                walked in steps of 32.  8 waves (2 per SIMD) in a 2 x 4
+//                grid; wave (wm, wn) owns the 32-row blocks b = 2*mb + wm and
+//                64 weight rows, i.e. (BM/64) x 2 tiles of
+//                v_mfma_f32_32x32x16_bf16 accumulators.
+//   persistent   one block per compute unit walks a fixed sequence of tiles
+//                of its XCD; the load pipeline runs on across tile borders,
+//                so a tile's first K steps arrive while the previous tile
+//                finishes, and the next tile's row lookup is done a tile
+//                ahead.
+//   loads        global -> LDS with buffer_load ... lds (no registers) into a
+//                4-slot ring of K steps, two steps in flight while one is
+//                computed; waves 0-3 move A rows, waves 4-7 weight rows.
+//                LDS rows are 64 bytes with XOR-swizzled 16-byte pieces so the
+//                fragment reads are free of bank conflicts.  One barrier per
+//                K step.  Tile-packed weights (moe_pack_ffn_weights) arrive
+//                as one contiguous 16 KB block per step.
+//   GEMM1        A rows are gathered from x through row_to_slot (expand); the
+//                256 weight rows are 128 gate rows and the matching 128 up
+//                rows interleaved in 32-row groups, so each lane holds a gate
+//                value and its up value and silu(g)*u is formed in registers
+//   GEMM2        A rows are act rows; 256 output columns per tile
 //   rows         32-row MFMA blocks past the tile's last valid row are skipped
 //
 // One expert's whole row set usually fits one M-tile (BM = 320 >= the
@@ -34,6 +44,7 @@ constexpr int kBK = kPanelK;     // K elements per step: 64 bytes of every A and
 constexpr int kBN = kPanelRows; // weight rows per block
 constexpr int kStages = 4;      // LDS ring: steps k+1, k+2 in flight while step k computes
 constexpr int kRowBytes = kBK * 2;
+constexpr int kGrid = 256;       // persistent blocks: one per compute unit
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -93,42 +104,102 @@ struct Units {
   static constexpr int MAXW = A > B ? A : B;
 };
 
-// The K loop of one block.  Every step each wave moves its units global ->
-// LDS with buffer_load ... lds (no registers): lane l of unit u fills LDS row
-// 16u + l/4, stored piece l%4.  Steps k+1 and k+2 stay in flight while step k
-// runs on the matrix cores; loads past the last step read an empty buffer
-// (all out of range: no memory traffic), so every step issues the same loads
-// and each wave's vmcnt arithmetic holds.
-// Wave (wm, wn) owns the 32-row A blocks b = 2*mb + wm and B rows
-// [64*wn, 64*wn + 64).  LIVE: A blocks of this wave holding valid rows; the
-// others issue no MFMAs.
+// Block -> tiles.  Workgroups are dispatched to the 8 XCDs round robin
+// (linear id % 8); block b walks tiles L = b, b + G, b + 2G, ... (G, the
+// grid, a multiple of 8), so all its tiles belong to XCD b % 8.  M-tiles are
+// dealt to XCDs round robin and, within an XCD, neighbouring tile indices
+// walk the N-tiles of one M-tile, so the blocks that share an A tile (the
+// expert's gathered rows) run together on one XCD and find it in that XCD's
+// L2; every weight panel is read by exactly one block.
+__device__ __forceinline__ void xcd_map(int L, int NT, int& mt, int& nt) {
+  const int xcd = L & 7, local = L >> 3;
+  mt = xcd + 8 * (local / NT);
+  nt = local % NT;
+}
+
+// What a block needs to stream one tile: the weight resource, this lane's
+// DMA source offsets (A rows for waves 0-3, weight rows for waves 4-7) and
+// the tile's rows.
+struct Tile {
+  __amdgpu_buffer_rsrc_t rb;
+  uint32_t src[5];
+  int row0, nrows, n0;
+  bool valid;
+};
+
+template <int MBW, bool GATED, bool PACKED>
+__device__ __forceinline__ void load_tile(Tile& t, int L, int NT, const uint16_t* __restrict__ W, int rows_e, int Fh,
+                                          int K, int topk, const int32_t* __restrict__ r2s,
+                                          const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+                                          int El, int wave, int lane) {
+  using U = Units<MBW>;
+  constexpr int BM = U::BM;
+  int mt, nt, e = 0, row0 = 0, nrows = 0;
+  xcd_map(L, NT, mt, nt);
+  t.valid = find_tile_t(counts, offsets, El, BM, mt, e, row0, nrows);
+  if (!t.valid) return;  // uniform
+  t.row0 = row0;
+  t.nrows = nrows;
+  t.n0 = nt * (GATED ? kBN / 2 : kBN);
+  t.rb = PACKED ? make_rsrc(W + ((int64_t)e * rows_e + (int64_t)nt * kBN) * K, (uint32_t)kBN * K * 2u)
+                : make_rsrc(W + (int64_t)e * rows_e * K, (uint32_t)rows_e * K * 2u);
+  // A rows past nrows get an offset beyond the A buffer's range (its size is
+  // below 2^31 and K offsets stay below 2^31): the range-checked load reads
+  // nothing for them.
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    uint32_t off = 0x80000000u;
+    if (wave < 4) {
+      const int R = (wave + 4 * i) * 16 + (lane >> 2);  // A row of the tile
+      if (i < U::A && R < nrows) {
+        const uint32_t row = GATED ? (uint32_t)(r2s[row0 + R] / topk) : (uint32_t)(row0 + R);
+        off = row * (uint32_t)K * 2u + (uint32_t)((lane & 3) ^ swz(R)) * 16u;
+      }
+    } else if (i < U::B) {
+      const int c = (wave - 4 + 4 * i) * 16 + (lane >> 2);  // weight row of the tile
+      if constexpr (PACKED) {
+        // a packed K-step block is the LDS image: unit u at u KB, lane at 16 B
+        off = (uint32_t)((wave - 4 + 4 * i) * 1024 + lane * 16);
+      } else {
+        const uint32_t wrow = GATED ? (uint32_t)panel_w1_row(c, nt, Fh) : (uint32_t)panel_w2_row(c, nt);
+        off = wrow * (uint32_t)K * 2u + (uint32_t)((lane & 3) ^ swz(BM + c)) * 16u;
+      }
+    }
+    t.src[i] = off;
+  }
+}
+
+// K loop of one tile: KT steps, global step counter g (ring slot g %
+// kStages).  At each step the loads of global step g + kStages - 1 are
+// issued: this tile's, the next tile's first steps, or (after the last tile)
+// loads of an empty buffer (all out of range: no memory traffic) so that
+// every step issues the same number of loads and each wave's vmcnt
+// arithmetic holds.  LIVE: A blocks of this wave holding valid rows.
 template <int MBW, int LIVE, bool PACKED>
-__device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                      __amdgpu_buffer_rsrc_t rz, const uint32_t* __restrict__ src,
-                                      uint8_t* __restrict__ lds, f32x16 (&acc)[MBW][2], int K, int wave, int lane,
-                                      int wm, int wn) {
+__device__ __forceinline__ void tile_kloop(const Tile& cur, const Tile& nxt, __amdgpu_buffer_rsrc_t ra,
+                                           __amdgpu_buffer_rsrc_t rz, uint8_t* __restrict__ lds,
+                                           f32x16 (&acc)[MBW][2], int KT, int& g, int wave, int lane, int wm,
+                                           int wn) {
   using U = Units<MBW>;
   constexpr int BM = U::BM;
   constexpr int STAGE = (BM + kBN) * kRowBytes;
-  const int KT = K / kBK;
   const bool a_wave = wave < 4;  // uniform
-  auto dma = [&](int slot, int kt) {
-    const bool real = kt < KT;
+  auto dma = [&](int slot, const Tile& t, int kt, bool real) {
     const int sk = real ? kt * kRowBytes : 0;
-    // packed weights: the next K step is the next contiguous block
     const int skb = real ? kt * (PACKED ? kBN * kRowBytes : kRowBytes) : 0;
     uint8_t* base = lds + slot * STAGE;
     if (a_wave) {
       const __amdgpu_buffer_rsrc_t r = real ? ra : rz;
 #pragma unroll
       for (int i = 0; i < U::A; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(base + (wave + 4 * i) * 1024), 16, src[i], sk, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(base + (wave + 4 * i) * 1024), 16, t.src[i], sk, 0,
+                                                 0);
     } else {
-      const __amdgpu_buffer_rsrc_t r = real ? rb : rz;
+      const __amdgpu_buffer_rsrc_t r = real ? t.rb : rz;
 #pragma unroll
       for (int i = 0; i < U::B; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(base + BM * kRowBytes + (wave - 4 + 4 * i) * 1024), 16,
-                                                 src[i], skb, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(base + BM * kRowBytes + (wave - 4 + 4 * i) * 1024),
+                                                 16, t.src[i], skb, 0, 0);
     }
   };
   // fragment addresses (bytes within a stage): lane l reads row R, logical
@@ -166,39 +237,21 @@ __device__ __forceinline__ void kloop(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer
         acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][mb], b[ks][1], acc[mb][1], 0, 0, 0);
       }
   };
-#pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) dma(s, s);
-  int slot = 0;
-  for (int kt = 0; kt < KT; ++kt) {
-    // own loads of step kt have landed once only the kStages-2 newer steps remain
+  for (int kt = 0; kt < KT; ++kt, ++g) {
+    // own loads of step g have landed once only the kStages-2 newer steps remain
     if (a_wave) __builtin_amdgcn_s_waitcnt(wait_vm((kStages - 2) * U::A));
     else __builtin_amdgcn_s_waitcnt(wait_vm((kStages - 2) * U::B));
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    // the slot read in step kt-1 is free: every wave has passed the barrier
-    const int fill = slot == 0 ? kStages - 1 : slot - 1;
-    dma(fill, kt + kStages - 1);
+    compute(g % kStages);
     __builtin_amdgcn_sched_barrier(0);
-    compute(slot);
-    slot = slot == kStages - 1 ? 0 : slot + 1;
+    // the slot read in step g-1 is free: every wave has passed the barrier
+    const int ahead = kt + kStages - 1;
+    const int fill = (g + kStages - 1) % kStages;
+    if (ahead < KT) dma(fill, cur, ahead, true);
+    else dma(fill, nxt, ahead - KT, nxt.valid);
   }
-  // drain the trailing (empty) loads before LDS is reused
-  __builtin_amdgcn_s_waitcnt(wait_vm(0));
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  __builtin_amdgcn_s_barrier();
-}
-
-// Block -> (M-tile, N-tile).  Workgroups are dispatched to the 8 XCDs round
-// robin (linear id % 8).  M-tiles are dealt to XCDs round robin too, and on
-// each XCD consecutive blocks walk the N-tiles of one M-tile, so the blocks
-// that share an A tile (the expert's gathered rows) run together on one XCD
-// and find it in that XCD's L2; every weight panel is still read by exactly
-// one block.
-__device__ __forceinline__ void xcd_map(int L, int NT, int& mt, int& nt) {
-  const int xcd = L & 7, local = L >> 3;
-  mt = xcd + 8 * (local / NT);
-  nt = local % NT;
 }
 
 // GATED = true : GEMM1 + silu_and_mul.  A = x [T, K] gathered by row_to_slot /
@@ -206,7 +259,7 @@ __device__ __forceinline__ void xcd_map(int L, int NT, int& mt, int& nt) {
 // GATED = false: GEMM2.  A = act [N, K] (grouped rows), W = W2 [El, Nw, K],
 //                out = y [N, Nw] (OT = bf16 bits or float).
 // PACKED: W is in the tile-packed layout (one contiguous 16 KB block per K
-// step of the block's panel), else row-major.
+// step of a tile's panel), else row-major.  K / 32 >= kStages - 1.
 template <int MBW, bool GATED, bool PACKED, typename OT>
 __global__ __launch_bounds__(kTThreads) void ffn_tiled_kernel(
     const uint16_t* __restrict__ A, int K, int topk, const int32_t* __restrict__ r2s, const uint16_t* __restrict__ W,
@@ -217,128 +270,100 @@ __global__ __launch_bounds__(kTThreads) void ffn_tiled_kernel(
   constexpr int RING = kStages * (BM + kBN) * kRowBytes;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[RING];
 
-  int mt, ntile;
-  xcd_map(blockIdx.x, NT, mt, ntile);
-  int e, row0, nrows;
-  if (!find_tile_t(counts, offsets, El, BM, mt, e, row0, nrows)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: resource choices stay scalar
   const int wm = wave >> 2, wn = wave & 3;
-  constexpr int OC = GATED ? kBN / 2 : kBN;  // output columns of the block
-  const int n0 = ntile * OC;                 // first act column (GEMM1) / output column (GEMM2)
-
-  // Source byte offsets of this lane's DMA rows (fixed for the whole loop;
-  // the K position is the scalar offset).  A rows past nrows get an offset
-  // beyond the buffer's range (a_bytes < 2^31, K offsets < 2^31): the
-  // range-checked load reads nothing for them.
   const int rows_e = GATED ? 2 * Fh : Nw;
+  const int KT = K / kBK;
+  const int G = gridDim.x;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, a_bytes);
-  const __amdgpu_buffer_rsrc_t rb =
-      PACKED ? make_rsrc(W + ((int64_t)e * rows_e + (int64_t)ntile * kBN) * K, (uint32_t)kBN * K * 2u)
-             : make_rsrc(W + (int64_t)e * rows_e * K, (uint32_t)rows_e * K * 2u);
   const __amdgpu_buffer_rsrc_t rz = make_rsrc(A, 0u);
-  uint32_t src[U::MAXW];
+
+  Tile cur, nxt;
+  int L = blockIdx.x;
+  load_tile<MBW, GATED, PACKED>(cur, L, NT, W, rows_e, Fh, K, topk, r2s, counts, offsets, El, wave, lane);
+  if (!cur.valid) return;  // uniform: the whole block has no tile
+  load_tile<MBW, GATED, PACKED>(nxt, L + G, NT, W, rows_e, Fh, K, topk, r2s, counts, offsets, El, wave, lane);
+
+  // prologue: the first kStages-1 steps of the first tile
+  {
+    constexpr int STAGE = (BM + kBN) * kRowBytes;
+    const bool a_wave = wave < 4;
 #pragma unroll
-  for (int i = 0; i < U::MAXW; ++i) {
-    if (wave < 4) {
-      const int R = (wave + 4 * i) * 16 + (lane >> 2);  // A row of the tile
-      const uint32_t piece = (uint32_t)((lane & 3) ^ swz(R)) * 16u;
-      if (i < U::A && R < nrows) {
-        const uint32_t row = GATED ? (uint32_t)(r2s[row0 + R] / topk) : (uint32_t)(row0 + R);
-        src[i] = row * (uint32_t)K * 2u + piece;
+    for (int s = 0; s < kStages - 1; ++s) {
+      uint8_t* base = lds + s * STAGE;
+      if (a_wave) {
+#pragma unroll
+        for (int i = 0; i < U::A; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(base + (wave + 4 * i) * 1024), 16, cur.src[i],
+                                                   s * kRowBytes, 0, 0);
       } else {
-        src[i] = 0x80000000u;
+#pragma unroll
+        for (int i = 0; i < U::B; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(cur.rb, (lds_ptr_t)(base + BM * kRowBytes + (wave - 4 + 4 * i) * 1024),
+                                                   16, cur.src[i], s * (PACKED ? kBN * kRowBytes : kRowBytes), 0, 0);
       }
-    } else {
-      const int c = (wave - 4 + 4 * i) * 16 + (lane >> 2);  // B row of the tile
-      uint32_t off;
-      if constexpr (PACKED) {
-        // a packed K-step block is the LDS image: unit u at u KB, lane at 16 B
-        off = (uint32_t)((wave - 4 + 4 * i) * 1024 + lane * 16);
-      } else {
-        const uint32_t piece = (uint32_t)((lane & 3) ^ swz(BM + c)) * 16u;
-        const uint32_t wrow = GATED ? (uint32_t)panel_w1_row(c, ntile, Fh) : (uint32_t)panel_w2_row(c, ntile);
-        off = wrow * (uint32_t)K * 2u + piece;
-      }
-      src[i] = i < U::B ? off : 0x80000000u;
     }
   }
 
-  f32x16 acc[MBW][2];
-#pragma unroll
-  for (int mb = 0; mb < MBW; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[mb][nb][j] = 0.0f;
-
-  // blocks b = 2*mb + wm with b*32 < nrows
-  int live = ((nrows + 31) / 32 - wm + 1) / 2;
-  live = live < 0 ? 0 : (live > MBW ? MBW : live);
-
-  switch (live) {
-    case 0: kloop<MBW, 0, PACKED>(ra, rb, rz, src, lds, acc, K, wave, lane, wm, wn); break;
-    case 1: kloop<MBW, 1, PACKED>(ra, rb, rz, src, lds, acc, K, wave, lane, wm, wn); break;
-    case 2: kloop<MBW, (MBW >= 2 ? 2 : MBW), PACKED>(ra, rb, rz, src, lds, acc, K, wave, lane, wm, wn); break;
-    case 3: kloop<MBW, (MBW >= 3 ? 3 : MBW), PACKED>(ra, rb, rz, src, lds, acc, K, wave, lane, wm, wn); break;
-    case 4: kloop<MBW, (MBW >= 4 ? 4 : MBW), PACKED>(ra, rb, rz, src, lds, acc, K, wave, lane, wm, wn); break;
-    default: kloop<MBW, MBW, PACKED>(ra, rb, rz, src, lds, acc, K, wave, lane, wm, wn); break;
-  }
-
-  // Epilogue.  acc[mb][nb][j] is C[row (j/4)*8 + (lane/32)*4 + j%4][col lane%32]
-  // of block b = 2*mb + wm.  bf16 results are staged through LDS (the K loop
-  // is done with it) so that global stores are whole 16-byte row pieces; the
-  // A blocks of the two wave rows go in two passes (b even, then b odd).
   const int cl = lane & 31;
-  if constexpr (GATED || sizeof(OT) == 2) {
-    constexpr int OS = OC + 8;  // padded LDS row (bf16 elements)
-    static_assert(MBW * 32 * OS * 2 <= RING, "staging tile fits in the LDS ring");
-    uint16_t* st = reinterpret_cast<uint16_t*>(lds);
-    constexpr int CPR = OC / 8;  // 16-byte pieces per row
-    uint16_t* ob = reinterpret_cast<uint16_t*>(out);
+  int g = 0;
+  while (true) {
+    f32x16 acc[MBW][2];
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      if (wm == pass) {
+    for (int mb = 0; mb < MBW; ++mb)
 #pragma unroll
-        for (int mb = 0; mb < MBW; ++mb) {
-          if (mb >= live) continue;
+      for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int r = mb * 32 + (j >> 2) * 8 + (lane >> 5) * 4 + (j & 3);  // row within this pass
-            if constexpr (GATED) {
-              const float g = acc[mb][0][j], u = acc[mb][1][j];
-              st[r * OS + wn * 32 + cl] = f32_to_bf16_bits(g / (1.0f + expf(-g)) * u);
-            } else {
-              st[r * OS + wn * 64 + cl] = f32_to_bf16_bits(acc[mb][0][j]);
-              st[r * OS + wn * 64 + 32 + cl] = f32_to_bf16_bits(acc[mb][1][j]);
-            }
-          }
-        }
-      }
-      __syncthreads();
-      // pass rows: blocks b = 2*mb + pass, b*32 < nrows
-      for (int p = tid; p < MBW * 32 * CPR; p += kTThreads) {
-        const int r = p / CPR, c8 = (p % CPR) * 8;
-        const int tr = (2 * (r >> 5) + pass) * 32 + (r & 31);  // row of the tile
-        if (tr < nrows)
-          *reinterpret_cast<u32x4*>(ob + (int64_t)(row0 + tr) * ldo + n0 + c8) =
-              *reinterpret_cast<const u32x4*>(st + r * OS + c8);
-      }
-      __syncthreads();
+        for (int j = 0; j < 16; ++j) acc[mb][nb][j] = 0.0f;
+    // blocks b = 2*mb + wm with b*32 < nrows
+    int live = ((cur.nrows + 31) / 32 - wm + 1) / 2;
+    live = live < 0 ? 0 : (live > MBW ? MBW : live);
+    switch (live) {
+      case 0: tile_kloop<MBW, 0, PACKED>(cur, nxt, ra, rz, lds, acc, KT, g, wave, lane, wm, wn); break;
+      case 1: tile_kloop<MBW, 1, PACKED>(cur, nxt, ra, rz, lds, acc, KT, g, wave, lane, wm, wn); break;
+      case 2: tile_kloop<MBW, (MBW >= 2 ? 2 : MBW), PACKED>(cur, nxt, ra, rz, lds, acc, KT, g, wave, lane, wm, wn); break;
+      case 3: tile_kloop<MBW, (MBW >= 3 ? 3 : MBW), PACKED>(cur, nxt, ra, rz, lds, acc, KT, g, wave, lane, wm, wn); break;
+      case 4: tile_kloop<MBW, (MBW >= 4 ? 4 : MBW), PACKED>(cur, nxt, ra, rz, lds, acc, KT, g, wave, lane, wm, wn); break;
+      default: tile_kloop<MBW, MBW, PACKED>(cur, nxt, ra, rz, lds, acc, KT, g, wave, lane, wm, wn); break;
     }
-  } else {
+
+    // Epilogue, straight from the accumulators (the LDS ring already holds
+    // the next tile's first steps).  acc[mb][nb][j] is C[row (j/4)*8 +
+    // (lane/32)*4 + j%4][col lane%32] of block b = 2*mb + wm; for each j the
+    // 32 lanes of a half-wave store 32 consecutive columns of one row.
 #pragma unroll
     for (int mb = 0; mb < MBW; ++mb) {
       if (mb >= live) continue;
+#pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int r = (2 * mb + wm) * 32 + (j >> 2) * 8 + (lane >> 5) * 4 + (j & 3);
-        if (r >= nrows) continue;
-        const int64_t orow = (int64_t)(row0 + r) * ldo;
+        if (r >= cur.nrows) continue;
+        const int64_t orow = (int64_t)(cur.row0 + r) * ldo;
+        if constexpr (GATED) {
+          const float gt = acc[mb][0][j], u = acc[mb][1][j];
+          reinterpret_cast<uint16_t*>(out)[orow + cur.n0 + wn * 32 + cl] =
+              f32_to_bf16_bits(gt / (1.0f + expf(-gt)) * u);
+        } else if constexpr (sizeof(OT) == 2) {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) out[orow + n0 + wn * 64 + nb * 32 + cl] = acc[mb][nb][j];
+          for (int nb = 0; nb < 2; ++nb)
+            reinterpret_cast<uint16_t*>(out)[orow + cur.n0 + wn * 64 + nb * 32 + cl] = f32_to_bf16_bits(acc[mb][nb][j]);
+        } else {
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) out[orow + cur.n0 + wn * 64 + nb * 32 + cl] = acc[mb][nb][j];
+        }
       }
     }
+
+    if (!nxt.valid) break;  // uniform
+    cur = nxt;
+    L += G;
+    load_tile<MBW, GATED, PACKED>(nxt, L + G, NT, W, rows_e, Fh, K, topk, r2s, counts, offsets, El, wave, lane);
   }
+  // drain the trailing (empty) loads before the block's LDS is released
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
 }
 
 template <int MBW, bool PACKED>
@@ -348,12 +373,17 @@ hipError_t launch_tiled_mbw(const uint16_t* x, int64_t T, int64_t N, int topk, i
   constexpr int BM = 64 * MBW;
   int64_t mtiles = (N + BM - 1) / BM + (N < El ? N : (int64_t)El);
   mtiles = (mtiles + 7) / 8 * 8;  // whole rounds of the 8 XCDs
-  const int nt1 = F / (kBN / 2), nt2 = H / kBN;  // 128 act columns / 256 output columns per block
-  hipLaunchKernelGGL((ffn_tiled_kernel<MBW, true, PACKED, uint16_t>), dim3((unsigned)(mtiles * nt1)), dim3(kTThreads),
-                     0, stream, x, H, topk, r2s, w1, 2 * F, F, counts, offsets, El, act, F, (uint32_t)(T * H * 2), nt1);
+  const int nt1 = F / (kBN / 2), nt2 = H / kBN;  // 128 act columns / 256 output columns per tile
+  // persistent grid: one block per compute unit, fewer if there are fewer tiles
+  auto grid = [&](int nt) {
+    const int64_t tiles = mtiles * nt;
+    return dim3((unsigned)(tiles < kGrid ? tiles : kGrid));
+  };
+  hipLaunchKernelGGL((ffn_tiled_kernel<MBW, true, PACKED, uint16_t>), grid(nt1), dim3(kTThreads), 0, stream, x, H,
+                     topk, r2s, w1, 2 * F, F, counts, offsets, El, act, F, (uint32_t)(T * H * 2), nt1);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const dim3 g2((unsigned)(mtiles * nt2));
+  const dim3 g2 = grid(nt2);
   const uint32_t act_bytes = (uint32_t)(N * F * 2);
   if (y_dtype == MOE_BF16)
     hipLaunchKernelGGL((ffn_tiled_kernel<MBW, false, PACKED, uint16_t>), g2, dim3(kTThreads), 0, stream, act, F, topk,
