@@ -18,8 +18,11 @@
 //   N <= 64         : one wavefront does everything (decode batches)
 //   N <= kSingleMax : one 1024-thread block does everything
 //   larger N        : count kernel (per block counts + in-block ranks, which
-//                     are parked in slot_to_row) -> one-block scan kernel
-//                     (per expert prefix over blocks, offsets) -> scatter
+//                     are parked in slot_to_row), then for up to 64 count
+//                     blocks one fused kernel in which every block sums the
+//                     block counts it needs itself and scatters, else a
+//                     one-block scan kernel (per expert prefix over blocks,
+//                     offsets) -> scatter
 #include "moe_internal.h"
 
 namespace moe {
@@ -284,6 +287,54 @@ __global__ __launch_bounds__(256) void compact_scatter_kernel(
   if (s >= R) r2s[s] = -1;
 }
 
+// Fused scan + scatter for few count blocks (B <= kFusedMaxBlocks): block b
+// (1024 threads, the same 1024 slots as count block b) sums every block's
+// counts per expert itself -- the total (for the expert offsets) and the part
+// of blocks before b (its base) -- so no separate scan pass is needed.
+// Block 0 writes counts and offsets.
+constexpr int kFusedMaxBlocks = 64;
+
+__global__ __launch_bounds__(kThreads) void compact_scan_scatter_kernel(
+    const int32_t* __restrict__ ids, int64_t N, const int32_t* __restrict__ emap, int Eg, int El,
+    const int32_t* __restrict__ block_counts /*[B][El]*/, int B, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ s2r, int32_t* __restrict__ r2s) {
+  extern __shared__ int lds[];
+  int* base = lds;          // [El]
+  int* tmp = base + El;     // [kWaves + 1]
+  const int b = blockIdx.x;
+  const int e = threadIdx.x;  // El <= kThreads: one expert per thread
+  int tot = 0, pre = 0;
+  if (e < El) {
+    for (int bb = 0; bb < B; ++bb) {
+      const int c = block_counts[(int64_t)bb * El + e];
+      tot += c;
+      pre += bb < b ? c : 0;
+    }
+  }
+  int total;
+  const int off = block_exclusive_scan(e < El ? tot : 0, tmp, &total);
+  if (e < El) {
+    base[e] = off + pre;
+    if (b == 0) {
+      counts[e] = tot;
+      offsets[e] = off;
+    }
+  }
+  if (b == 0 && e == 0) offsets[El] = total;
+  __syncthreads();
+  const int64_t s = (int64_t)b * kBlockSlots + threadIdx.x;
+  if (s < N) {
+    const int l = local_of(ids[s], emap, Eg, El);
+    int row = -1;
+    if (l >= 0) {
+      row = base[l] + s2r[s];  // in-block rank parked by the count kernel
+      r2s[row] = (int32_t)s;
+    }
+    s2r[s] = row;
+    if (s >= total) r2s[s] = -1;
+  }
+}
+
 }  // namespace
 
 size_t route_compact_workspace_bytes(int64_t N, int E_local) {
@@ -312,6 +363,12 @@ hipError_t launch_route_compact(const int32_t* ids, int64_t N, const int32_t* em
                      sizeof(int) * (size_t)kWaves * El, stream, ids, N, emap, Eg, El, bc, s2r);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (B <= kFusedMaxBlocks) {
+    hipLaunchKernelGGL(compact_scan_scatter_kernel, dim3((unsigned)B), dim3(kThreads),
+                       sizeof(int) * ((size_t)El + kWaves + 1), stream, ids, N, emap, Eg, El, bc, (int)B, counts,
+                       offsets, s2r, r2s);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(compact_scan_kernel, dim3(1), dim3(kThreads),
                      sizeof(int) * ((size_t)El + El + 1 + kWaves + 1), stream, bc, (int)B, El, counts,
                      offsets);
