@@ -221,7 +221,7 @@ def traffic_for(name):
 # secondary: gate throughput with rotating buffers
 
 
-def bench_gate(dev, E, reps):
+def bench_gate(dev, E, reps, scoring="softmax"):
     import torch
 
     import mixture_experts_routing_amd as moe
@@ -236,14 +236,16 @@ def bench_gate(dev, E, reps):
         bufs.append((lb, torch.empty((T, K), dtype=torch.float32, device=dev),
                      torch.empty((T, K), dtype=torch.int32, device=dev), torch.empty((T, K), dtype=torch.int32, device=dev)))
 
+    fn = moe.moe_topk_softmax if scoring == "softmax" else moe.moe_topk_sigmoid
+
     def calls():
         for b in bufs:
-            moe.moe_topk_softmax(b[0], K, False, b[1], b[2], b[3])
+            fn(b[0], K, False, b[1], b[2], b[3])
 
     ms = graph_ms(calls, max(1, reps // nbuf), dev) / nbuf
     nbytes = T * E * 2 + T * K * 12
     gbs = nbytes / (ms / 1e3) / 1e9
-    return {"E": E, "T": T, "K": K, "ms": round(ms, 5), "mrows_per_s": round(T / (ms / 1e3) / 1e6, 1),
+    return {"scoring": scoring, "E": E, "T": T, "K": K, "ms": round(ms, 5), "mrows_per_s": round(T / (ms / 1e3) / 1e6, 1),
             "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_call": nbytes}
 
 
@@ -380,8 +382,9 @@ def main():
     if not args.no_secondary:
         reps = 50 if args.quick else 400
         secondary["gate"] = [bench_gate(dev, E, reps) for E in (128, 160)]
+        secondary["gate"] += [bench_gate(dev, E, reps, "sigmoid") for E in (128, 160, 256)]
         for g in secondary["gate"]:
-            log(f"[bench] gate E={g['E']}: {g['ms'] * 1e3:.2f} us, {g['mrows_per_s']} Mrows/s, "
+            log(f"[bench] gate {g['scoring']} E={g['E']}: {g['ms'] * 1e3:.2f} us, {g['mrows_per_s']} Mrows/s, "
                 f"{g['gbs']} GB/s ({100 * g['hbm_frac']:.1f}% of HBM)")
         secondary["decode"] = bench_decode(dev, 5 if args.quick else 20)
     cpu = None

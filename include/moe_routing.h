@@ -79,6 +79,21 @@ int moe_topk_softmax(const void* logits, int logits_dtype, int64_t T, int32_t E,
                      int32_t* token_expert_indices, void* stream);
 
 /*
+ * moe_topk_sigmoid -- the sigmoid-scoring variant of the gate.
+ * Source: page "Upstream Reference: Deep-Spark xllm + vllm", section "File
+ * Index" (a sigmoid/softmax top-k dispatcher and a sigmoid variant of the
+ * kernel for DeepSeek-style routing).  The page names the variant without
+ * defining it; this library's reading: every expert is scored independently
+ * by s_j = 1 / (1 + exp(-logit_j)); the top-K experts are those with the
+ * largest scores (the logit order, s being increasing; ties -> lower expert
+ * index), in descending order; weight_k = s_{id_k}, or with renormalize
+ * s_{id_k} / sum_k' s_{id_k'}.  No score bias and no expert groups.
+ * Arguments, layout, limits and errors are exactly those of moe_topk_softmax.
+ */
+int moe_topk_sigmoid(const void* logits, int logits_dtype, int64_t T, int32_t E, int32_t K, int32_t renormalize,
+                     float* topk_weights, int32_t* topk_ids, int32_t* token_expert_indices, void* stream);
+
+/*
  * moe_route_compact -- route compaction for one expert-parallel rank.
  * Source: b70-optimization-lab note "MTP1 M2 compact scheduler closure"
  * (2026-07-16), design paragraph: derive each local expert's row count and

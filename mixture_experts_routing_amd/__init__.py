@@ -19,7 +19,7 @@ _LIB = _lib.load()
 
 __all__ = [
     "moe_topk_softmax", "moe_route_compact", "moe_grouped_ffn", "moe_combine", "moe_layer",
-    "MOE_F32", "MOE_BF16", "MOE_MXFP4", "MOE_BF16_TILED", "moe_pack_ffn_weights", "MoeError", "library_path",
+    "MOE_F32", "MOE_BF16", "MOE_MXFP4", "MOE_BF16_TILED", "moe_pack_ffn_weights", "moe_topk_sigmoid", "MoeError", "library_path",
 ]
 
 
@@ -72,11 +72,7 @@ def _stream(stream, device) -> int:
     return stream.cuda_stream
 
 
-def moe_topk_softmax(logits: torch.Tensor, K: int, renormalize: bool = False,
-                     topk_weights: Optional[torch.Tensor] = None, topk_ids: Optional[torch.Tensor] = None,
-                     token_expert_indices: Optional[torch.Tensor] = None, with_indices: bool = True,
-                     stream=None) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
-    """logits [T, E] (f32 or bf16) -> (weights f32 [T,K], ids i32 [T,K], token_expert_indices i32 [T,K])."""
+def _gate(fn_name, logits, K, renormalize, topk_weights, topk_ids, token_expert_indices, with_indices, stream):
     dev = _dev(logits)
     T, E = logits.shape
     if topk_weights is None:
@@ -86,10 +82,28 @@ def moe_topk_softmax(logits: torch.Tensor, K: int, renormalize: bool = False,
     if token_expert_indices is None and with_indices:
         token_expert_indices = torch.empty((T, K), dtype=torch.int32, device=dev)
     _dev(topk_weights, topk_ids, token_expert_indices)
-    _check(_LIB.moe_topk_softmax(_ptr(logits), _dt(logits), T, E, K, int(bool(renormalize)), _ptr(topk_weights),
-                                 _ptr(topk_ids), _ptr(token_expert_indices), _stream(stream, dev)),
-           "moe_topk_softmax")
+    _check(getattr(_LIB, fn_name)(_ptr(logits), _dt(logits), T, E, K, int(bool(renormalize)), _ptr(topk_weights),
+                                  _ptr(topk_ids), _ptr(token_expert_indices), _stream(stream, dev)), fn_name)
     return topk_weights, topk_ids, token_expert_indices
+
+
+def moe_topk_softmax(logits: torch.Tensor, K: int, renormalize: bool = False,
+                     topk_weights: Optional[torch.Tensor] = None, topk_ids: Optional[torch.Tensor] = None,
+                     token_expert_indices: Optional[torch.Tensor] = None, with_indices: bool = True,
+                     stream=None) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
+    """logits [T, E] (f32 or bf16) -> (weights f32 [T,K], ids i32 [T,K], token_expert_indices i32 [T,K])."""
+    return _gate("moe_topk_softmax", logits, K, renormalize, topk_weights, topk_ids, token_expert_indices,
+                 with_indices, stream)
+
+
+def moe_topk_sigmoid(logits: torch.Tensor, K: int, renormalize: bool = False,
+                     topk_weights: Optional[torch.Tensor] = None, topk_ids: Optional[torch.Tensor] = None,
+                     token_expert_indices: Optional[torch.Tensor] = None, with_indices: bool = True,
+                     stream=None) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
+    """Sigmoid-scoring gate: same arguments and outputs as moe_topk_softmax,
+    weight = sigmoid(logit) of each chosen expert (optionally renormalised)."""
+    return _gate("moe_topk_sigmoid", logits, K, renormalize, topk_weights, topk_ids, token_expert_indices,
+                 with_indices, stream)
 
 
 def route_compact_workspace_bytes(T: int, K: int, E_local: int) -> int:

@@ -1,6 +1,9 @@
 """Builds libmoe_routing.so (all HIP kernels + the C ABI) for gfx950 in-tree.
 
-    python -m mixture_experts_routing_amd.build [-v]
+    python mixture_experts_routing_amd/build.py [-v]
+
+(run as a file: importing the package itself loads the library, which may
+not exist yet or may be stale).
 
 Each translation unit is compiled with hipcc in parallel into _build/, then
 linked into mixture_experts_routing_amd/libmoe_routing.so.  Always rebuilds.

@@ -34,15 +34,32 @@ const char* moe_status_string(int s) {
 
 int moe_last_hip_error(void) { return g_last_hip_error; }
 
-int moe_topk_softmax(const void* logits, int logits_dtype, int64_t T, int32_t E, int32_t K, int32_t renormalize,
-                     float* topk_weights, int32_t* topk_ids, int32_t* token_expert_indices, void* stream) {
+namespace {
+int check_gate(const void* logits, int logits_dtype, int64_t T, int32_t E, int32_t K, const float* topk_weights,
+               const int32_t* topk_ids) {
   if (T < 0 || E < 1 || K < 1 || K > E) return MOE_ERR_INVALID_ARG;
   if (logits_dtype != MOE_F32 && logits_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (E > 1280 || K > 32) return MOE_ERR_UNSUPPORTED;
   if (T > ((int64_t)1 << 31) / K) return MOE_ERR_UNSUPPORTED;  // k*T + t must fit int32
-  if (T == 0) return MOE_OK;
+  if (T == 0) return -1;                                        // valid no-op
   if (!logits || !topk_weights || !topk_ids) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+}  // namespace
+
+int moe_topk_softmax(const void* logits, int logits_dtype, int64_t T, int32_t E, int32_t K, int32_t renormalize,
+                     float* topk_weights, int32_t* topk_ids, int32_t* token_expert_indices, void* stream) {
+  const int st = check_gate(logits, logits_dtype, T, E, K, topk_weights, topk_ids);
+  if (st != MOE_OK) return st < 0 ? MOE_OK : st;
   return hip_status(moe::launch_topk_softmax(logits, logits_dtype, T, E, K, renormalize != 0, topk_weights, topk_ids,
+                                             token_expert_indices, static_cast<hipStream_t>(stream)));
+}
+
+int moe_topk_sigmoid(const void* logits, int logits_dtype, int64_t T, int32_t E, int32_t K, int32_t renormalize,
+                     float* topk_weights, int32_t* topk_ids, int32_t* token_expert_indices, void* stream) {
+  const int st = check_gate(logits, logits_dtype, T, E, K, topk_weights, topk_ids);
+  if (st != MOE_OK) return st < 0 ? MOE_OK : st;
+  return hip_status(moe::launch_topk_sigmoid(logits, logits_dtype, T, E, K, renormalize != 0, topk_weights, topk_ids,
                                              token_expert_indices, static_cast<hipStream_t>(stream)));
 }
 

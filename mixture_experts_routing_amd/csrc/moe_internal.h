@@ -117,6 +117,9 @@ __device__ __forceinline__ float group_sum_f32(float x) {
 hipError_t launch_topk_softmax(const void* logits, int logits_dtype, int64_t T, int E, int K,
                                int renormalize, float* w, int32_t* ids, int32_t* tei,
                                hipStream_t stream);
+hipError_t launch_topk_sigmoid(const void* logits, int logits_dtype, int64_t T, int E, int K,
+                               int renormalize, float* w, int32_t* ids, int32_t* tei,
+                               hipStream_t stream);
 
 size_t route_compact_workspace_bytes(int64_t N, int E_local);
 hipError_t launch_route_compact(const int32_t* topk_ids, int64_t N, const int32_t* expert_map,

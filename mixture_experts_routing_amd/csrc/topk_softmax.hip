@@ -156,7 +156,8 @@ __device__ __forceinline__ void load_row_chunk(const LT* __restrict__ row, int j
 
 constexpr int kBlock = 256;
 
-template <typename LT, int G, int V, int KMAX>
+// SIG: sigmoid scoring -- weight = sigmoid(logit), no softmax denominator.
+template <typename LT, int G, int V, int KMAX, bool SIG>
 __global__ __launch_bounds__(kBlock) void topk_softmax_kernel(
     const LT* __restrict__ logits, int64_t T, int E, int K, int renorm, int vec_ok,
     float* __restrict__ w_out, int32_t* __restrict__ id_out, int32_t* __restrict__ tei_out) {
@@ -210,19 +211,22 @@ __global__ __launch_bounds__(kBlock) void topk_softmax_kernel(
   // softmax denominator: fixed-order pairwise tree inside the lane, then the
   // DPP group sum
   const float mx = Tr::value(top[0]);
-  constexpr float kLog2e = 1.4426950408889634f;
-  float ex[V];
+  float denom = 1.0f;
+  if constexpr (!SIG) {
+    constexpr float kLog2e = 1.4426950408889634f;
+    float ex[V];
 #pragma unroll
-  for (int i = 0; i < V; ++i) {
-    const float v = Tr::to_f32(raw[i]);
-    ex[i] = (row_ok && j0 + i < E) ? __builtin_amdgcn_exp2f((v - mx) * kLog2e) : 0.0f;
+    for (int i = 0; i < V; ++i) {
+      const float v = Tr::to_f32(raw[i]);
+      ex[i] = (row_ok && j0 + i < E) ? __builtin_amdgcn_exp2f((v - mx) * kLog2e) : 0.0f;
+    }
+#pragma unroll
+    for (int w = 1; w < V; w <<= 1) {
+#pragma unroll
+      for (int i = 0; i + w < V; i += 2 * w) ex[i] += ex[i + w];
+    }
+    denom = group_sum_f32<G>(ex[0]);
   }
-#pragma unroll
-  for (int w = 1; w < V; w <<= 1) {
-#pragma unroll
-    for (int i = 0; i + w < V; i += 2 * w) ex[i] += ex[i + w];
-  }
-  const float denom = group_sum_f32<G>(ex[0]);
 
   // each lane finishes ranks lane_g, lane_g + G, ...
   Key mine[RPL];
@@ -235,11 +239,13 @@ __global__ __launch_bounds__(kBlock) void topk_softmax_kernel(
     for (int r = c * G; r < (c + 1) * G && r < KMAX; ++r) kk = (lane_g + c * G == r) ? top[r] : kk;
     mine[c] = kk;
     const int q = lane_g + c * G;
-    e_mine[c] = (q < K) ? expf(Tr::value(kk) - mx) : 0.0f;
+    if constexpr (SIG) e_mine[c] = (q < K) ? 1.0f / (1.0f + expf(-Tr::value(kk))) : 0.0f;
+    else e_mine[c] = (q < K) ? expf(Tr::value(kk) - mx) : 0.0f;
     part += e_mine[c];
   }
   float norm = denom;
   if (renorm) norm = group_sum_f32<G>(part);
+  (void)mx;
 
   if (row_ok) {
 #pragma unroll
@@ -247,7 +253,7 @@ __global__ __launch_bounds__(kBlock) void topk_softmax_kernel(
       const int q = lane_g + c * G;
       if (q < K) {
         const int64_t o = t * K + q;
-        w_out[o] = e_mine[c] / norm;
+        w_out[o] = (SIG && !renorm) ? e_mine[c] : e_mine[c] / norm;
         id_out[o] = Tr::index(mine[c]);
         if (tei_out) tei_out[o] = (int32_t)((int64_t)q * T + t);
       }
@@ -255,7 +261,7 @@ __global__ __launch_bounds__(kBlock) void topk_softmax_kernel(
   }
 }
 
-template <typename LT, int G, int V, int KMAX>
+template <typename LT, int G, int V, int KMAX, bool SIG>
 hipError_t launch_cfg(const LT* logits, int64_t T, int E, int K, int renorm, float* w, int32_t* ids,
                       int32_t* tei, hipStream_t stream) {
   constexpr int ROWS = kBlock / G;
@@ -266,15 +272,15 @@ hipError_t launch_cfg(const LT* logits, int64_t T, int E, int K, int renorm, flo
   const int vec_bytes = (elt == 2) ? ((V % 8 == 0) ? 16 : 8) : 16;
   const bool vec_ok = ((E * elt) % vec_bytes == 0) && ((V * elt) % vec_bytes == 0) &&
                       ((uintptr_t)logits % vec_bytes == 0);
-  hipLaunchKernelGGL((topk_softmax_kernel<LT, G, V, KMAX>), dim3((unsigned)blocks), dim3(kBlock), 0,
+  hipLaunchKernelGGL((topk_softmax_kernel<LT, G, V, KMAX, SIG>), dim3((unsigned)blocks), dim3(kBlock), 0,
                      stream, logits, T, E, K, renorm, (int)vec_ok, w, ids, tei);
   return hipGetLastError();
 }
 
-template <typename LT, int KMAX>
+template <typename LT, int KMAX, bool SIG>
 hipError_t dispatch_gv(const LT* logits, int64_t T, int E, int K, int renorm, float* w, int32_t* ids,
                        int32_t* tei, hipStream_t stream) {
-#define MOE_GATE_CASE(GG, VV) return launch_cfg<LT, GG, VV, KMAX>(logits, T, E, K, renorm, w, ids, tei, stream)
+#define MOE_GATE_CASE(GG, VV) return launch_cfg<LT, GG, VV, KMAX, SIG>(logits, T, E, K, renorm, w, ids, tei, stream)
   if (E <= 8) MOE_GATE_CASE(1, 8);
   if (E <= 16) MOE_GATE_CASE(1, 16);
   if (E <= 20) MOE_GATE_CASE(1, 20);
@@ -331,7 +337,7 @@ __device__ __forceinline__ void merge_top8(int32_t* a, const int32_t* b, int nb)
   cx(a[0], a[1]); cx(a[2], a[3]); cx(a[4], a[5]); cx(a[6], a[7]);
 }
 
-template <int V>
+template <int V, bool SIG>
 __global__ __launch_bounds__(kBlock) void topk8_bf16_kernel(const uint16_t* __restrict__ logits, int64_t T, int K,
                                                             int renorm, float* __restrict__ w_out,
                                                             int32_t* __restrict__ id_out,
@@ -415,44 +421,51 @@ __global__ __launch_bounds__(kBlock) void topk8_bf16_kernel(const uint16_t* __re
 
   // softmax denominator over the lane's V values, pairwise, then the group
   const float mx = Keys<uint16_t>::value(top[0]);
-  constexpr float kLog2e = 1.4426950408889634f;
-  float ex[V];
+  float denom = 1.0f;
+  if constexpr (!SIG) {
+    constexpr float kLog2e = 1.4426950408889634f;
+    float ex[V];
 #pragma unroll
-  for (int i = 0; i < W; ++i) {
-    ex[2 * i] = __builtin_amdgcn_exp2f((__uint_as_float(wd[i] << 16) - mx) * kLog2e);
-    ex[2 * i + 1] = __builtin_amdgcn_exp2f((__uint_as_float(wd[i] & 0xFFFF0000u) - mx) * kLog2e);
+    for (int i = 0; i < W; ++i) {
+      ex[2 * i] = __builtin_amdgcn_exp2f((__uint_as_float(wd[i] << 16) - mx) * kLog2e);
+      ex[2 * i + 1] = __builtin_amdgcn_exp2f((__uint_as_float(wd[i] & 0xFFFF0000u) - mx) * kLog2e);
+    }
+#pragma unroll
+    for (int w = 1; w < V; w <<= 1) {
+#pragma unroll
+      for (int i = 0; i + w < V; i += 2 * w) ex[i] += ex[i + w];
+    }
+    denom = group_sum_f32<G>(ex[0]);
   }
-#pragma unroll
-  for (int w = 1; w < V; w <<= 1) {
-#pragma unroll
-    for (int i = 0; i + w < V; i += 2 * w) ex[i] += ex[i + w];
-  }
-  const float denom = group_sum_f32<G>(ex[0]);
 
   // lane q finishes rank q
   int32_t mine = top[0];
 #pragma unroll
   for (int r = 1; r < 8; ++r) mine = (q == r) ? top[r] : mine;
-  const float e = (q < K) ? expf(Keys<uint16_t>::value(mine) - mx) : 0.0f;
+  const float v = Keys<uint16_t>::value(mine);
+  float e;
+  if constexpr (SIG) e = (q < K) ? 1.0f / (1.0f + expf(-v)) : 0.0f;
+  else e = (q < K) ? expf(v - mx) : 0.0f;
   const float norm = renorm ? group_sum_f32<G>(e) : denom;
   if (row_ok && q < K) {
     const int64_t o = t * K + q;
-    w_out[o] = e / norm;
+    w_out[o] = (SIG && !renorm) ? e : e / norm;
     id_out[o] = Keys<uint16_t>::index(mine);
     if (tei_out) tei_out[o] = (int32_t)((int64_t)q * T + t);
   }
 }
 
-template <int V>
+template <int V, bool SIG>
 hipError_t launch_fast(const uint16_t* logits, int64_t T, int K, int renorm, float* w, int32_t* ids, int32_t* tei,
                        hipStream_t stream) {
   const int64_t blocks = (T + (kBlock / 8) - 1) / (kBlock / 8);
-  hipLaunchKernelGGL((topk8_bf16_kernel<V>), dim3((unsigned)blocks), dim3(kBlock), 0, stream, logits, T, K, renorm, w,
+  hipLaunchKernelGGL((topk8_bf16_kernel<V, SIG>), dim3((unsigned)blocks), dim3(kBlock), 0, stream, logits, T, K, renorm, w,
                      ids, tei);
   return hipGetLastError();
 }
 
 // E = 8*V with V in {8, 12, 16, 20, 24}, K <= 8, aligned rows: the fast kernel
+template <bool SIG>
 bool try_fast(const uint16_t* logits, int64_t T, int E, int K, int renorm, float* w, int32_t* ids, int32_t* tei,
               hipStream_t stream, hipError_t* err) {
   if (K > 8 || E % 8 != 0) return false;
@@ -460,29 +473,41 @@ bool try_fast(const uint16_t* logits, int64_t T, int E, int K, int renorm, float
   const int align = (V % 8 == 0) ? 16 : 8;
   if ((uintptr_t)logits % align != 0 || (E * 2) % align != 0) return false;
   switch (V) {
-    case 8: *err = launch_fast<8>(logits, T, K, renorm, w, ids, tei, stream); return true;
-    case 12: *err = launch_fast<12>(logits, T, K, renorm, w, ids, tei, stream); return true;
-    case 16: *err = launch_fast<16>(logits, T, K, renorm, w, ids, tei, stream); return true;
-    case 20: *err = launch_fast<20>(logits, T, K, renorm, w, ids, tei, stream); return true;
-    case 24: *err = launch_fast<24>(logits, T, K, renorm, w, ids, tei, stream); return true;
+    case 8: *err = launch_fast<8, SIG>(logits, T, K, renorm, w, ids, tei, stream); return true;
+    case 12: *err = launch_fast<12, SIG>(logits, T, K, renorm, w, ids, tei, stream); return true;
+    case 16: *err = launch_fast<16, SIG>(logits, T, K, renorm, w, ids, tei, stream); return true;
+    case 20: *err = launch_fast<20, SIG>(logits, T, K, renorm, w, ids, tei, stream); return true;
+    case 24: *err = launch_fast<24, SIG>(logits, T, K, renorm, w, ids, tei, stream); return true;
     default: return false;
   }
 }
 }  // namespace
 
-hipError_t launch_topk_softmax(const void* logits, int logits_dtype, int64_t T, int E, int K,
-                               int renormalize, float* w, int32_t* ids, int32_t* tei,
-                               hipStream_t stream) {
+namespace {
+template <bool SIG>
+hipError_t launch_gate(const void* logits, int logits_dtype, int64_t T, int E, int K, int renormalize, float* w,
+                       int32_t* ids, int32_t* tei, hipStream_t stream) {
   if (logits_dtype == MOE_BF16) {
     const uint16_t* p = static_cast<const uint16_t*>(logits);
     hipError_t err;
-    if (try_fast(p, T, E, K, renormalize, w, ids, tei, stream, &err)) return err;
-    return K <= 8 ? dispatch_gv<uint16_t, 8>(p, T, E, K, renormalize, w, ids, tei, stream)
-                  : dispatch_gv<uint16_t, 32>(p, T, E, K, renormalize, w, ids, tei, stream);
+    if (try_fast<SIG>(p, T, E, K, renormalize, w, ids, tei, stream, &err)) return err;
+    return K <= 8 ? dispatch_gv<uint16_t, 8, SIG>(p, T, E, K, renormalize, w, ids, tei, stream)
+                  : dispatch_gv<uint16_t, 32, SIG>(p, T, E, K, renormalize, w, ids, tei, stream);
   }
   const float* p = static_cast<const float*>(logits);
-  return K <= 8 ? dispatch_gv<float, 8>(p, T, E, K, renormalize, w, ids, tei, stream)
-                : dispatch_gv<float, 32>(p, T, E, K, renormalize, w, ids, tei, stream);
+  return K <= 8 ? dispatch_gv<float, 8, SIG>(p, T, E, K, renormalize, w, ids, tei, stream)
+                : dispatch_gv<float, 32, SIG>(p, T, E, K, renormalize, w, ids, tei, stream);
+}
+}  // namespace
+
+hipError_t launch_topk_softmax(const void* logits, int logits_dtype, int64_t T, int E, int K, int renormalize,
+                               float* w, int32_t* ids, int32_t* tei, hipStream_t stream) {
+  return launch_gate<false>(logits, logits_dtype, T, E, K, renormalize, w, ids, tei, stream);
+}
+
+hipError_t launch_topk_sigmoid(const void* logits, int logits_dtype, int64_t T, int E, int K, int renormalize,
+                               float* w, int32_t* ids, int32_t* tei, hipStream_t stream) {
+  return launch_gate<true>(logits, logits_dtype, T, E, K, renormalize, w, ids, tei, stream);
 }
 
 }  // namespace moe

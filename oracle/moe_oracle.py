@@ -48,7 +48,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "decode_bf16", "decode_mxfp4", "decode_weights", "topk_softmax", "route_compact",
+    "decode_bf16", "decode_mxfp4", "decode_weights", "topk_softmax", "topk_sigmoid", "route_compact",
     "tile_owners", "silu", "ffn_route", "ffn_rows", "grouped_ffn", "grouped_ffn_rows",
     "combine", "moe_layer", "E2M1_VALUES",
 ]
@@ -128,6 +128,32 @@ def topk_softmax(logits, K: int, renormalize: bool, logits_dtype: str = "f32"):
     order = np.lexsort((j, -v), axis=-1)
     ids = order[:, :K].astype(np.int32)
     w = np.take_along_axis(p, ids.astype(np.int64), axis=1)
+    if renormalize:
+        w = w / w.sum(axis=1, keepdims=True)
+    tei = (np.arange(K, dtype=np.int64)[None, :] * T + np.arange(T, dtype=np.int64)[:, None]).astype(np.int32)
+    return w, ids, tei
+
+
+def topk_sigmoid(logits, K: int, renormalize: bool, logits_dtype: str = "f32"):
+    """Sigmoid-scoring gate ([UR] "File Index": a sigmoid variant of the
+    top-k kernel for DeepSeek-style routing, named but not defined there).
+
+    Reading: each expert is scored on its own, s_j = 1 / (1 + exp(-v_j)); the
+    K best scores (= the K largest logits, s being increasing; equal logits ->
+    lower index first) are chosen in descending order; weights[t,k] =
+    s[ids[t,k]], divided by the sum of the row's K chosen scores when
+    renormalize is set.  Returns (weights float64, ids int32, token_expert_
+    indices int32) like topk_softmax."""
+    v = _as_f64(logits, logits_dtype)
+    T, E = v.shape
+    assert 1 <= K <= E
+    assert np.all(np.isfinite(v)), "logits must be finite"
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-v))
+    j = np.broadcast_to(np.arange(E), v.shape)
+    order = np.lexsort((j, -v), axis=-1)
+    ids = order[:, :K].astype(np.int32)
+    w = np.take_along_axis(s, ids.astype(np.int64), axis=1)
     if renormalize:
         w = w / w.sum(axis=1, keepdims=True)
     tei = (np.arange(K, dtype=np.int64)[None, :] * T + np.arange(T, dtype=np.int64)[:, None]).astype(np.int32)

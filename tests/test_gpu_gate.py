@@ -17,11 +17,13 @@ pytestmark = pytest.mark.gpu
 W_RTOL = 1e-6
 
 
-def check_gate(logits_host, dtype, K, renorm, tag=""):
+def check_gate(logits_host, dtype, K, renorm, tag="", scoring="softmax"):
     T, E = logits_host.shape
-    w_ref, ids_ref, tei_ref = oracle.topk_softmax(logits_host, K, renorm, dtype)
-    print(f"[gate] {tag} T={T} E={E} K={K} renorm={renorm} dtype={dtype}", flush=True)
-    w, ids, tei = moe.moe_topk_softmax(dev_any(logits_host, dtype), K, renorm)
+    ref_fn = oracle.topk_softmax if scoring == "softmax" else oracle.topk_sigmoid
+    gpu_fn = moe.moe_topk_softmax if scoring == "softmax" else moe.moe_topk_sigmoid
+    w_ref, ids_ref, tei_ref = ref_fn(logits_host, K, renorm, dtype)
+    print(f"[gate] {scoring} {tag} T={T} E={E} K={K} renorm={renorm} dtype={dtype}", flush=True)
+    w, ids, tei = gpu_fn(dev_any(logits_host, dtype), K, renorm)
     torch.cuda.synchronize()
     ids = host_i(ids)
     bad = np.flatnonzero((ids != ids_ref).any(axis=1))
@@ -109,3 +111,33 @@ def test_gate_empty():
     x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
     w, ids, tei = moe.moe_topk_softmax(x, 4, False)
     assert w.shape == (0, 4)
+
+
+# ---------------------------------------------------------------------------
+# sigmoid scoring: same selection, weight = sigmoid(logit) (renormalised on request)
+
+
+@pytest.mark.parametrize("E", [128, 160, 256])
+@pytest.mark.parametrize("renorm", [False, True])
+def test_sigmoid_gate_full(E, renorm):
+    c = synth.gate_case(E, T=65536, K=8, seed=1, renormalize=renorm)
+    check_gate(c.logits, "bf16", 8, renorm, "full", "sigmoid")
+
+
+@pytest.mark.parametrize("E", [1, 3, 8, 17, 40, 64, 96, 192, 333, 1280])
+def test_sigmoid_gate_sweep(E):
+    rng = np.random.default_rng(500 + E)
+    for K in sorted({min(E, k) for k in (1, 2, 6, 8, 9, 32)}):
+        logits = synth.gate_logits_bf16(97, E, seed=E * 7 + K, tie_fraction=0.3)
+        check_gate(logits, "bf16", K, bool(rng.integers(2)), "sweep", "sigmoid")
+        f = (rng.integers(-4, 5, size=(61, E)) * 0.5).astype(np.float32)
+        check_gate(f, "f32", K, bool(K % 2), "f32ties", "sigmoid")
+
+
+def test_sigmoid_gate_extremes():
+    E, K = 64, 8
+    rows = [np.zeros(E, np.float32), np.linspace(-90, 90, E).astype(np.float32),
+            np.full(E, -87.0, np.float32), np.full(E, 30.0, np.float32)]
+    f = np.stack(rows)
+    check_gate(f, "f32", K, False, "extremes", "sigmoid")
+    check_gate(f, "f32", K, True, "extremes", "sigmoid")

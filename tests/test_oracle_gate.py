@@ -142,3 +142,56 @@ def test_injected_ties_present():
     v = c.logits
     n_tie_rows = sum(len(np.unique(v[t])) < v.shape[1] for t in range(0, 65536, 64))
     assert n_tie_rows > 0
+
+
+# ---------------------------------------------------------------------------
+# sigmoid-scoring gate
+
+
+def test_sigmoid_ids_equal_softmax_ids():
+    # the sigmoid and the softmax are both increasing in the logit, so the
+    # chosen experts (already pinned by brute force) must be identical
+    rng = np.random.default_rng(21)
+    for E, K in ((8, 2), (40, 6), (128, 8), (160, 8)):
+        x = (rng.integers(-3, 4, size=(300, E)) * 0.5).astype(np.float32)  # many ties
+        _, ids_s, tei_s = oracle.topk_sigmoid(x, K, False)
+        _, ids_m, tei_m = oracle.topk_softmax(x, K, False)
+        assert np.array_equal(ids_s, ids_m) and np.array_equal(tei_s, tei_m)
+
+
+def test_sigmoid_closed_forms():
+    x = np.array([[0.0, np.log(3.0), -np.log(3.0), -5.0]], dtype=np.float64)
+    w, ids, _ = oracle.topk_sigmoid(x, 2, False, "f32")
+    assert ids.tolist() == [[1, 0]]
+    assert w[0, 0] == pytest.approx(0.75, abs=1e-15) and w[0, 1] == 0.5
+    w, _, _ = oracle.topk_sigmoid(x, 2, True, "f32")
+    assert w[0].tolist() == pytest.approx([0.6, 0.4], abs=1e-15)
+
+
+def test_sigmoid_symmetry_and_independence():
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((50, 16)) * 3
+    w_pos, ids, _ = oracle.topk_sigmoid(x, 16, False, "f32")
+    # with K = E every expert is chosen: s(x) + s(-x) = 1 for each of them
+    w_neg, ids_n, _ = oracle.topk_sigmoid(-x, 16, False, "f32")
+    sp = np.zeros_like(x)
+    sn = np.zeros_like(x)
+    np.put_along_axis(sp, ids.astype(np.int64), w_pos, axis=1)
+    np.put_along_axis(sn, ids_n.astype(np.int64), w_neg, axis=1)
+    assert np.allclose(sp + sn, 1.0, atol=1e-15)
+    # unlike the softmax, a chosen weight does not depend on the other logits
+    w1, ids1, _ = oracle.topk_sigmoid(x, 4, False, "f32")
+    y = x.copy()
+    for t in range(x.shape[0]):
+        others = np.setdiff1d(np.arange(16), ids1[t])
+        y[t, others] -= 1.0  # lower the losers: same winners
+    w2, ids2, _ = oracle.topk_sigmoid(y, 4, False, "f32")
+    assert np.array_equal(ids1, ids2) and np.array_equal(w1, w2)
+
+
+def test_sigmoid_renormalised_sums_to_one():
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal((200, 64)).astype(np.float32) * 2
+    w, _, _ = oracle.topk_sigmoid(x, 8, True)
+    assert np.allclose(w.sum(axis=1), 1.0, atol=1e-14)
+    assert np.all(np.diff(w, axis=1) <= 0)
