@@ -328,6 +328,38 @@ def bench_decode(dev, reps):
 
 
 # ---------------------------------------------------------------------------
+# secondary: block-aligned layout (moe_route_align)
+
+
+def bench_align(dev, reps):
+    import numpy as np
+    import torch
+
+    import mixture_experts_routing_amd as moe
+    import synth
+
+    out = []
+    for name, T, K, Eg, El, bs in (("prefill", 4096, 8, 128, 128, 128), ("decode", 2, 6, 256, 40, 16)):
+        rng = np.random.default_rng(0)
+        emap = None if El == Eg else i32_dev(synth.contiguous_expert_map(Eg, El), dev)
+        ids = [i32_dev(rng.integers(0, Eg, size=(T, K)), dev) for _ in range(8)]
+        N = T * K
+        res = (torch.empty(El + 1, dtype=torch.int32, device=dev),
+               torch.empty(N + El * (bs - 1), dtype=torch.int32, device=dev),
+               torch.empty(-(-N // bs) + El, dtype=torch.int32, device=dev),
+               torch.empty(N, dtype=torch.int32, device=dev))
+        ws = torch.empty(moe.route_align_workspace_bytes(T, K, El), dtype=torch.uint8, device=dev)
+
+        def calls():
+            for i in ids:
+                moe.moe_route_align(i, emap, El, bs, E_global=Eg, out=res, workspace=ws)
+
+        ms = graph_ms(calls, reps, dev) / len(ids)
+        out.append({"workload": name, "T": T, "K": K, "E_local": El, "block": bs, "ms": round(ms, 5)})
+    return out
+
+
+# ---------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the prefill workload
 
 
@@ -387,6 +419,10 @@ def main():
             log(f"[bench] gate {g['scoring']} E={g['E']}: {g['ms'] * 1e3:.2f} us, {g['mrows_per_s']} Mrows/s, "
                 f"{g['gbs']} GB/s ({100 * g['hbm_frac']:.1f}% of HBM)")
         secondary["decode"] = bench_decode(dev, 5 if args.quick else 20)
+        secondary["route_align"] = bench_align(dev, 5 if args.quick else 20)
+        for a in secondary["route_align"]:
+            log(f"[bench] route_align {a['workload']} (T={a['T']}, K={a['K']}, E_local={a['E_local']}, "
+                f"block {a['block']}): {a['ms'] * 1e3:.2f} us")
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")

@@ -121,6 +121,34 @@ int moe_route_compact(const int32_t* topk_ids, int64_t T, int32_t K, const int32
 size_t moe_route_compact_workspace_bytes(int64_t T, int32_t K, int32_t E_local);
 
 /*
+ * moe_route_align -- block-aligned (padded) variant of the expert-grouped
+ * layout, for grouped GEMMs that work on fixed-height row blocks.
+ * Source: page "Upstream Reference: Deep-Spark xllm + vllm", section "File
+ * Index" (a block-alignment kernel for the scatter; named, not defined).
+ * Reading: the rows of moe_route_compact, each local expert's rows starting
+ * on a multiple of block_size, the unused tail rows of an expert's last block
+ * being padding.  N = T*K slots;
+ *   cap_rows   = N + E_local * (block_size - 1)
+ *   cap_blocks = ceil(N / block_size) + E_local
+ * Outputs (device, int32, caller-allocated):
+ *   padded_offsets [E_local+1]  expert e owns padded rows
+ *                               [padded_offsets[e], padded_offsets[e+1]),
+ *                               = counts rounded up to block_size, scanned
+ *   sorted_slots   [cap_rows]   slot of each padded row in slot order within
+ *                               an expert; -1 for padding and past the end
+ *   block_expert   [cap_blocks] local expert of each block; -1 past the end
+ *   slot_to_row    [N]          padded row of each slot; -1 for remote slots
+ * workspace: moe_route_align_workspace_bytes(T, K, E_local) bytes, 16-byte
+ * aligned (the compaction's own arrays live there).
+ * Limits: 1 <= block_size <= 4096, E_local <= 768, cap_rows < 2^31.
+ */
+int moe_route_align(const int32_t* topk_ids, int64_t T, int32_t K, const int32_t* expert_map,
+                    int32_t E_global, int32_t E_local, int32_t block_size, int32_t* padded_offsets,
+                    int32_t* sorted_slots, int32_t* block_expert, int32_t* slot_to_row, void* workspace,
+                    size_t workspace_bytes, void* stream);
+size_t moe_route_align_workspace_bytes(int64_t T, int32_t K, int32_t E_local);
+
+/*
  * moe_grouped_ffn -- expert-grouped SwiGLU FFN over the compacted rows.
  * Sources: page "Upstream Reference: Deep-Spark xllm + vllm", section "File
  * Index" (expand -> gemm1 -> act (silu_and_mul) -> gemm2); b70 lab note

@@ -19,7 +19,7 @@ _LIB = _lib.load()
 
 __all__ = [
     "moe_topk_softmax", "moe_route_compact", "moe_grouped_ffn", "moe_combine", "moe_layer",
-    "MOE_F32", "MOE_BF16", "MOE_MXFP4", "MOE_BF16_TILED", "moe_pack_ffn_weights", "moe_topk_sigmoid", "MoeError", "library_path",
+    "MOE_F32", "MOE_BF16", "MOE_MXFP4", "MOE_BF16_TILED", "moe_pack_ffn_weights", "moe_topk_sigmoid", "moe_route_align", "MoeError", "library_path",
 ]
 
 
@@ -134,6 +134,36 @@ def moe_route_compact(topk_ids: torch.Tensor, expert_map: Optional[torch.Tensor]
                                   _ptr(offsets), _ptr(s2r), _ptr(r2s), _ptr(workspace), ws_bytes,
                                   _stream(stream, dev)), "moe_route_compact")
     return counts, offsets, s2r, r2s
+
+
+def route_align_workspace_bytes(T: int, K: int, E_local: int) -> int:
+    return int(_LIB.moe_route_align_workspace_bytes(T, K, E_local))
+
+
+def moe_route_align(topk_ids: torch.Tensor, expert_map: Optional[torch.Tensor], E_local: int, block_size: int,
+                    E_global: Optional[int] = None, out=None, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Block-aligned layout: -> (padded_offsets [E_local+1], sorted_slots [cap_rows],
+    block_expert [cap_blocks], slot_to_row [T*K]), all int32 (see moe_route_align)."""
+    dev = _dev(topk_ids, expert_map)
+    T, K = topk_ids.shape
+    N = T * K
+    if E_global is None:
+        E_global = expert_map.numel() if expert_map is not None else E_local
+    cap_rows = N + E_local * (block_size - 1)
+    cap_blocks = -(-N // block_size) + E_local
+    if out is None:
+        out = (torch.empty(E_local + 1, dtype=torch.int32, device=dev),
+               torch.empty(cap_rows, dtype=torch.int32, device=dev),
+               torch.empty(cap_blocks, dtype=torch.int32, device=dev),
+               torch.empty(N, dtype=torch.int32, device=dev))
+    poff, sorted_slots, block_expert, s2r = out
+    need = route_align_workspace_bytes(T, K, E_local)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _check(_LIB.moe_route_align(_ptr(topk_ids), T, K, _ptr(expert_map), E_global, E_local, block_size, _ptr(poff),
+                                _ptr(sorted_slots), _ptr(block_expert), _ptr(s2r), _ptr(workspace),
+                                workspace.numel(), _stream(stream, dev)), "moe_route_align")
+    return poff, sorted_slots, block_expert, s2r
 
 
 def grouped_ffn_workspace_bytes(T: int, K: int, H: int, F: int, E_local: int, w_dtype: int) -> int:

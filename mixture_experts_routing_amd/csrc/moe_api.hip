@@ -85,6 +85,31 @@ int moe_route_compact(const int32_t* topk_ids, int64_t T, int32_t K, const int32
                                               slot_to_row, row_to_slot, workspace, static_cast<hipStream_t>(stream)));
 }
 
+size_t moe_route_align_workspace_bytes(int64_t T, int32_t K, int32_t E_local) {
+  if (T < 0 || K <= 0 || E_local <= 0) return 0;
+  return moe::route_align_workspace_bytes(T * K, E_local);
+}
+
+int moe_route_align(const int32_t* topk_ids, int64_t T, int32_t K, const int32_t* expert_map, int32_t E_global,
+                    int32_t E_local, int32_t block_size, int32_t* padded_offsets, int32_t* sorted_slots,
+                    int32_t* block_expert, int32_t* slot_to_row, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  if (T < 0 || K < 1 || E_local < 1 || E_global < 1 || E_local > E_global) return MOE_ERR_INVALID_ARG;
+  if (block_size < 1) return MOE_ERR_INVALID_ARG;
+  if (!expert_map && E_local != E_global) return MOE_ERR_INVALID_ARG;
+  if (E_local > 768 || block_size > 4096) return MOE_ERR_UNSUPPORTED;
+  const int64_t N = T * K;
+  if (N + (int64_t)E_local * (block_size - 1) >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  if (!padded_offsets || !sorted_slots || !block_expert) return MOE_ERR_INVALID_ARG;
+  if (N > 0 && (!topk_ids || !slot_to_row)) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe::route_align_workspace_bytes(N, E_local);
+  if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_route_align(topk_ids, N, expert_map, E_global, E_local, block_size, padded_offsets,
+                                            sorted_slots, block_expert, slot_to_row, workspace,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 size_t moe_grouped_ffn_workspace_bytes(int64_t T, int32_t K, int32_t H, int32_t F, int32_t E_local, int w_dtype) {
   if (T <= 0 || K <= 0 || F <= 0 || H <= 0 || E_local <= 0) return 0;
   return moe::grouped_ffn_workspace_bytes(T * K, H, F, E_local, w_dtype);

@@ -127,6 +127,11 @@ hipError_t launch_route_compact(const int32_t* topk_ids, int64_t N, const int32_
                                 int32_t* slot_to_row, int32_t* row_to_slot, void* workspace,
                                 hipStream_t stream);
 
+size_t route_align_workspace_bytes(int64_t N, int E_local);
+hipError_t launch_route_align(const int32_t* topk_ids, int64_t N, const int32_t* expert_map, int E_global,
+                              int E_local, int block_size, int32_t* padded_offsets, int32_t* sorted_slots,
+                              int32_t* block_expert, int32_t* slot_to_row, void* workspace, hipStream_t stream);
+
 size_t grouped_ffn_workspace_bytes(int64_t N, int H, int F, int El, int w_dtype);
 hipError_t launch_grouped_ffn(const void* x, int x_dtype, int64_t T, int K, int H, int F,
                               int E_local, const void* w1, const uint8_t* w1s, const void* w2,

@@ -335,7 +335,105 @@ __global__ __launch_bounds__(kThreads) void compact_scan_scatter_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// block-aligned layout, from the compaction's counts / offsets / permutation
+
+// Expert e with off[e] <= x < off[e+1] (off ascending, off[0] = 0, x < off[El]).
+__device__ __forceinline__ int expert_at(const int32_t* __restrict__ off, int El, int x) {
+  int lo = 0, hi = El;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (off[mid] <= x) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// One block: padded offsets (exclusive scan of the counts rounded up to the
+// block size) and the expert of every block.
+__global__ __launch_bounds__(kThreads) void align_offsets_kernel(const int32_t* __restrict__ counts, int El, int bs,
+                                                                 int cap_blocks, int32_t* __restrict__ poff,
+                                                                 int32_t* __restrict__ block_expert) {
+  extern __shared__ int lds[];
+  int* off = lds;        // [El + 1]
+  int* tmp = off + El + 1;  // [kWaves + 1]
+  const int e = threadIdx.x;  // El <= kThreads
+  const int padded = e < El ? (counts[e] + bs - 1) / bs * bs : 0;
+  int total;
+  const int ex = block_exclusive_scan(padded, tmp, &total);
+  if (e < El) {
+    off[e] = ex;
+    poff[e] = ex;
+  }
+  if (e == 0) {
+    off[El] = total;
+    poff[El] = total;
+  }
+  __syncthreads();
+  const int nblocks = total / bs;
+  for (int b = threadIdx.x; b < cap_blocks; b += kThreads)
+    block_expert[b] = b < nblocks ? expert_at(off, El, b * bs) : -1;
+}
+
+// sorted_slots over the capacity and the padded row of every slot.
+__global__ __launch_bounds__(256) void align_fill_kernel(const int32_t* __restrict__ counts,
+                                                         const int32_t* __restrict__ offsets,
+                                                         const int32_t* __restrict__ r2s,
+                                                         const int32_t* __restrict__ s2r,
+                                                         const int32_t* __restrict__ poff, int El, int64_t N,
+                                                         int64_t cap_rows, int32_t* __restrict__ sorted_slots,
+                                                         int32_t* __restrict__ slot_to_row) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < cap_rows) {
+    const int p = (int)i;
+    int v = -1;
+    if (p < poff[El]) {
+      const int e = expert_at(poff, El, p);
+      const int o = p - poff[e];
+      if (o < counts[e]) v = r2s[offsets[e] + o];
+    }
+    sorted_slots[p] = v;
+  }
+  if (i < N) {
+    const int r = s2r[i];
+    int v = -1;
+    if (r >= 0) {
+      const int e = expert_at(offsets, El, r);
+      v = poff[e] + (r - offsets[e]);
+    }
+    slot_to_row[i] = v;
+  }
+}
+
 }  // namespace
+
+size_t route_align_workspace_bytes(int64_t N, int E_local) {
+  // counts, offsets, slot_to_row, row_to_slot of the compaction, then its workspace
+  const size_t own = ((size_t)(2 * E_local + 1) + 2 * (size_t)N) * sizeof(int32_t);
+  return (own + 255) / 256 * 256 + route_compact_workspace_bytes(N, E_local);
+}
+
+hipError_t launch_route_align(const int32_t* ids, int64_t N, const int32_t* emap, int Eg, int El, int bs,
+                              int32_t* poff, int32_t* sorted_slots, int32_t* block_expert, int32_t* slot_to_row,
+                              void* workspace, hipStream_t stream) {
+  int32_t* counts = static_cast<int32_t*>(workspace);
+  int32_t* offsets = counts + El;
+  int32_t* s2r = offsets + El + 1;
+  int32_t* r2s = s2r + N;
+  const size_t own = ((size_t)(2 * El + 1) + 2 * (size_t)N) * sizeof(int32_t);
+  void* cws = static_cast<uint8_t*>(workspace) + (own + 255) / 256 * 256;
+  hipError_t err = launch_route_compact(ids, N, emap, Eg, El, counts, offsets, s2r, r2s, cws, stream);
+  if (err != hipSuccess) return err;
+  const int64_t cap_rows = N + (int64_t)El * (bs - 1);
+  const int64_t cap_blocks = (N + bs - 1) / bs + El;
+  hipLaunchKernelGGL(align_offsets_kernel, dim3(1), dim3(kThreads), sizeof(int) * ((size_t)El + 1 + kWaves + 1),
+                     stream, counts, El, bs, (int)cap_blocks, poff, block_expert);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  const int64_t n = cap_rows > N ? cap_rows : N;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(align_fill_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, counts, offsets, r2s,
+                     s2r, poff, El, N, cap_rows, sorted_slots, slot_to_row);
+  return hipGetLastError();
+}
 
 size_t route_compact_workspace_bytes(int64_t N, int E_local) {
   if (N <= kSingleMax) return 0;

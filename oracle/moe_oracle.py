@@ -48,7 +48,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "decode_bf16", "decode_mxfp4", "decode_weights", "topk_softmax", "topk_sigmoid", "route_compact",
+    "decode_bf16", "decode_mxfp4", "decode_weights", "topk_softmax", "topk_sigmoid", "route_compact", "route_align", "route_align_capacity",
     "tile_owners", "silu", "ffn_route", "ffn_rows", "grouped_ffn", "grouped_ffn_rows",
     "combine", "moe_layer", "E2M1_VALUES",
 ]
@@ -200,6 +200,50 @@ def route_compact(topk_ids, expert_map, E_local: int):
     slot_to_row[grouped] = np.arange(R)
     return (counts.astype(np.int32), offsets.astype(np.int32),
             slot_to_row.astype(np.int32), row_to_slot.astype(np.int32))
+
+
+def route_align_capacity(N: int, E_local: int, block_size: int):
+    """Sizes the block-aligned layout can reach: padded rows and blocks."""
+    return N + E_local * (block_size - 1), -(-N // block_size) + E_local
+
+
+def route_align(topk_ids, expert_map, E_local: int, block_size: int):
+    """Block-aligned (padded) variant of the expert-grouped layout ([UR] "File
+    Index": a block-alignment kernel for the scatter).  Reading: every local
+    expert's rows, in the same slot order as route_compact, start on a
+    multiple of block_size; the unused tail rows of an expert's last block
+    are padding.
+
+    Returns padded_offsets [E_local+1] (expert e owns padded rows
+    [padded_offsets[e], padded_offsets[e+1]), a multiple of block_size
+    apart), sorted_slots [cap_rows] (slot of each padded row, -1 for padding
+    and past the end), block_expert [cap_blocks] (local expert of each
+    block, -1 past the end) and slot_to_row [N] (padded row of each slot, -1
+    for remote slots), all int32; the capacities come from
+    route_align_capacity."""
+    ids = np.asarray(topk_ids, dtype=np.int64).reshape(-1)
+    N = ids.size
+    counts, offsets, slot_to_row, row_to_slot = route_compact(ids, expert_map, E_local)
+    bs = int(block_size)
+    counts = counts.astype(np.int64)
+    offsets = offsets.astype(np.int64)
+    padded = -(-counts // bs) * bs
+    poff = np.zeros(E_local + 1, dtype=np.int64)
+    poff[1:] = np.cumsum(padded)
+    cap_rows, cap_blocks = route_align_capacity(N, E_local, bs)
+    sorted_slots = np.full(cap_rows, -1, dtype=np.int64)
+    block_expert = np.full(cap_blocks, -1, dtype=np.int64)
+    for e in range(E_local):
+        sorted_slots[poff[e]:poff[e] + counts[e]] = row_to_slot[offsets[e]:offsets[e + 1]]
+        block_expert[poff[e] // bs:poff[e + 1] // bs] = e
+    s2r = slot_to_row.astype(np.int64)
+    out_rows = np.full(N, -1, dtype=np.int64)
+    local = np.flatnonzero(s2r >= 0)
+    if local.size:
+        e_of = np.searchsorted(offsets, s2r[local], side="right") - 1
+        out_rows[local] = poff[e_of] + (s2r[local] - offsets[e_of])
+    return (poff.astype(np.int32), sorted_slots.astype(np.int32), block_expert.astype(np.int32),
+            out_rows.astype(np.int32))
 
 
 def tile_owners(topk_ids, expert_map, E_local: int, BM: int):

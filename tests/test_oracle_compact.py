@@ -153,3 +153,64 @@ def test_identity_map_equals_explicit_identity():
     b = oracle.route_compact(ids, np.arange(16, dtype=np.int32), 16)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+# ---------------------------------------------------------------------------
+# block-aligned (padded) layout
+
+
+def test_align_hand_example():
+    # "same" pattern: local experts 3, 17, 29 with 2 rows each; blocks of 4
+    emap = synth.contiguous_expert_map(256, 40)
+    inv = np.flatnonzero(emap >= 0)
+    rows = [[3, None, 17, None, 29, None]] * 2
+    remote = np.flatnonzero(emap < 0)[0]
+    ids = np.array([[inv[l] if l is not None else remote for l in r] for r in rows], np.int32)
+    poff, sorted_slots, block_expert, s2r = oracle.route_align(ids, emap, 40, 4)
+    want_poff = [0] * 4 + [4] * 14 + [8] * 12 + [12] * 11
+    assert poff.tolist() == want_poff
+    assert sorted_slots[:12].tolist() == [0, 6, -1, -1, 2, 8, -1, -1, 4, 10, -1, -1]
+    assert np.all(sorted_slots[12:] == -1) and sorted_slots.size == 12 + 40 * 3
+    assert block_expert[:3].tolist() == [3, 17, 29] and np.all(block_expert[3:] == -1)
+    assert s2r.tolist() == [0, -1, 4, -1, 8, -1, 1, -1, 5, -1, 9, -1]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_align_block_size_one_is_compaction(seed):
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(0, 64, size=(37, 6)).astype(np.int32)
+    emap = synth.random_expert_map(64, 20, seed=seed)
+    counts, offsets, s2r_c, r2s_c = oracle.route_compact(ids, emap, 20)
+    poff, sorted_slots, block_expert, s2r = oracle.route_align(ids, emap, 20, 1)
+    R = int(offsets[-1])
+    assert np.array_equal(poff, offsets) and np.array_equal(s2r, s2r_c)
+    assert np.array_equal(sorted_slots[:R], r2s_c[:R]) and np.all(sorted_slots[R:] == -1)
+    assert np.array_equal(block_expert[:R], np.repeat(np.arange(20), counts))
+
+
+@pytest.mark.parametrize("bs", [2, 8, 16, 64])
+def test_align_invariants(bs):
+    rng = np.random.default_rng(bs)
+    N_tok, K, Eg, El = 300, 8, 128, 48
+    ids = rng.integers(0, Eg, size=(N_tok, K)).astype(np.int32)
+    emap = synth.random_expert_map(Eg, El, seed=bs)
+    poff, sorted_slots, block_expert, s2r = oracle.route_align(ids, emap, El, bs)
+    loc = emap[ids.reshape(-1)]
+    total = int(poff[-1])
+    assert total % bs == 0 and np.all(np.diff(poff) % bs == 0)
+    # every local slot exactly once, at the row slot_to_row names
+    placed = sorted_slots[sorted_slots >= 0]
+    assert np.array_equal(np.sort(placed), np.flatnonzero(loc >= 0))
+    for s in np.flatnonzero(loc >= 0):
+        assert sorted_slots[s2r[s]] == s
+    assert np.all(s2r[loc < 0] == -1)
+    # each block holds one expert's slots, padding only after them, slot order kept
+    for b in range(total // bs):
+        e = block_expert[b]
+        seg = sorted_slots[b * bs:(b + 1) * bs]
+        real = seg[seg >= 0]
+        assert np.all(loc[real] == e)
+        assert np.all(np.diff(real) > 0)
+        k = real.size
+        assert np.all(seg[:k] >= 0) and np.all(seg[k:] == -1)
+    assert np.all(block_expert[total // bs:] == -1)
