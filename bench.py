@@ -107,6 +107,36 @@ def graph_ms(fn, reps, dev):
     return ms
 
 
+def ab_graph_ms(fa, fb, reps, dev):
+    """A/B timing: fa() and fb() captured in one graph each, replays
+    alternated (A, B, A, B, ...), each replay between two events; returns
+    the median milliseconds of each."""
+    import statistics
+
+    import torch
+
+    graphs = []
+    for f in (fa, fb):
+        f()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            f()
+        g.replay()
+        torch.cuda.synchronize()
+        graphs.append(g)
+    s = torch.cuda.current_stream(dev)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+          for _ in range(2)]
+    for r in range(reps):
+        for i, g in enumerate(graphs):
+            ev[i][r][0].record(s)
+            g.replay()
+            ev[i][r][1].record(s)
+    torch.cuda.synchronize()
+    return [statistics.median(a.elapsed_time(b) for a, b in ev[i]) for i in range(2)]
+
+
 # ---------------------------------------------------------------------------
 # main workload: the prefill layer
 
@@ -311,11 +341,24 @@ def bench_decode(dev, reps):
         t_ffn = graph_ms(each(ffn), reps, dev) / nvar
         t_cmb = graph_ms(each(combine), reps, dev) / nvar
         t_layer = graph_ms(each(compact, ffn, combine), reps, dev) / nvar
+        # A/B against the generic persistent scheduler (atomic work counter
+        # over every local expert, 64-column N tiles), alternated replays
+        cws = torch.empty(moe.grouped_ffn_control_workspace_bytes(T, K, H, F, El, moe.MOE_BF16), dtype=torch.uint8,
+                          device=dev)
+
+        def ffn_control(v):
+            counts, offsets, _, r2s = outs[v]
+            moe.moe_grouped_ffn_control(x, K, w1, w2, counts, offsets, r2s, y=y, workspace=cws)
+
+        t_a, t_b = ab_graph_ms(each(compact, ffn, combine), each(compact, ffn_control, combine), reps, dev)
+        t_a, t_b = t_a / nvar, t_b / nvar
         n_exp = len({l for r in synth.DECODE_PATTERNS[pat] for l in r if l is not None})
         wbytes = n_exp * (2 * F * H + H * F) * 2
         d = {"layer_ms": round(t_layer, 4), "compact_ms": round(t_cmp, 4), "ffn_ms": round(t_ffn, 4),
              "combine_ms": round(t_cmb, 4), "tokens_per_s": round(T / (t_layer / 1e3), 1),
-             "local_experts": n_exp, "weight_bytes": wbytes}
+             "local_experts": n_exp, "weight_bytes": wbytes,
+             "ab_layer_ms": {"compact": round(t_a, 4), "generic_control": round(t_b, 4)},
+             "projected_saved_ms_43_layers": round((t_b - t_a) * 43, 4)}
         if wbytes:
             gbs = wbytes / (t_ffn / 1e3) / 1e9
             d.update({"ffn_weight_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
@@ -323,8 +366,11 @@ def bench_decode(dev, reps):
         log(f"[bench] decode {pat}: " + json.dumps(d))
     nonempty = [p for p in res if res[p]["local_experts"] > 0]
     worst = min(nonempty, key=lambda p: res[p]["hbm_frac"])
+    saved = {p: res[p]["projected_saved_ms_43_layers"] for p in res}
     return {"patterns": res, "min_hbm_frac_pattern": worst, "min_hbm_frac": res[worst]["hbm_frac"],
-            "min_tokens_per_s": min(res[p]["tokens_per_s"] for p in res)}
+            "min_tokens_per_s": min(res[p]["tokens_per_s"] for p in res),
+            "scheduler_ab": {"min_projected_saved_ms_43_layers": min(saved.values()),
+                             "min_pattern": min(saved, key=saved.get)}}
 
 
 # ---------------------------------------------------------------------------

@@ -187,6 +187,27 @@ size_t moe_grouped_ffn_workspace_bytes(int64_t T, int32_t K, int32_t H, int32_t 
                                        int w_dtype);
 
 /*
+ * moe_grouped_ffn_control -- the same FFN as moe_grouped_ffn, run by the
+ * generic persistent scheduler that the b70 lab note "MTP1 M2 compact
+ * scheduler closure" measures its compact scheduler against (timing
+ * paragraph): one block per compute unit claims work items (local expert, N
+ * tile of 64 columns) from a global atomic counter, scanning every local
+ * expert whether or not any route reached it.  Kept as an A/B control for
+ * the compact path; the outputs agree with moe_grouped_ffn within rounding.
+ * Arguments as for moe_grouped_ffn; pairs (BF16, BF16) and (BF16, MXFP4);
+ * H % 64 == 0, F % 64 == 0.  workspace:
+ * moe_grouped_ffn_control_workspace_bytes(...) (the act rows and the two
+ * work counters, which the call resets itself).
+ */
+int moe_grouped_ffn_control(const void* x, int x_dtype, int64_t T, int32_t K, int32_t H, int32_t F,
+                            int32_t E_local, const void* w1, const uint8_t* w1_scale, const void* w2,
+                            const uint8_t* w2_scale, int w_dtype, const int32_t* counts,
+                            const int32_t* offsets, const int32_t* row_to_slot, void* y, int y_dtype,
+                            void* workspace, size_t workspace_bytes, void* stream);
+size_t moe_grouped_ffn_control_workspace_bytes(int64_t T, int32_t K, int32_t H, int32_t F,
+                                               int32_t E_local, int w_dtype);
+
+/*
  * moe_pack_ffn_weights -- store bf16 expert weights in the tile-packed layout
  * (MOE_BF16_TILED) that the many-rows-per-expert FFN kernels stream with
  * contiguous loads.  A one-time transform of the weights (model load), not

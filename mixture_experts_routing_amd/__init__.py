@@ -19,7 +19,7 @@ _LIB = _lib.load()
 
 __all__ = [
     "moe_topk_softmax", "moe_route_compact", "moe_grouped_ffn", "moe_combine", "moe_layer",
-    "MOE_F32", "MOE_BF16", "MOE_MXFP4", "MOE_BF16_TILED", "moe_pack_ffn_weights", "moe_topk_sigmoid", "moe_route_align", "MoeError", "library_path",
+    "MOE_F32", "MOE_BF16", "MOE_MXFP4", "MOE_BF16_TILED", "moe_pack_ffn_weights", "moe_topk_sigmoid", "moe_route_align", "moe_grouped_ffn_control", "MoeError", "library_path",
 ]
 
 
@@ -217,6 +217,35 @@ def moe_grouped_ffn(x: torch.Tensor, K: int, w1: torch.Tensor, w2: torch.Tensor,
                                 _ptr(w2_scale), w_dt, _ptr(counts), _ptr(offsets), _ptr(row_to_slot), _ptr(y),
                                 _dt(y), _ptr(workspace), workspace.numel(), _stream(stream, dev)),
            "moe_grouped_ffn")
+    return y
+
+
+def grouped_ffn_control_workspace_bytes(T: int, K: int, H: int, F: int, E_local: int, w_dtype: int) -> int:
+    return int(_LIB.moe_grouped_ffn_control_workspace_bytes(T, K, H, F, E_local, w_dtype))
+
+
+def moe_grouped_ffn_control(x: torch.Tensor, K: int, w1: torch.Tensor, w2: torch.Tensor, counts: torch.Tensor,
+                            offsets: torch.Tensor, row_to_slot: torch.Tensor, w1_scale=None, w2_scale=None,
+                            y_dtype: Optional[torch.dtype] = None, y: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None, stream=None):
+    """moe_grouped_ffn run by the generic atomic-counter scheduler (the A/B
+    control); same arguments and result layout."""
+    dev = _dev(x, w1, w2, counts, offsets, row_to_slot, w1_scale, w2_scale)
+    T, H = x.shape
+    E_local = w1.shape[0]
+    if w1.dtype == torch.uint8:
+        w_dt, F = MOE_MXFP4, w2.shape[2] * 2
+    else:
+        w_dt, F = _dt(w1), w2.shape[2]
+    if y is None:
+        y = torch.empty((T * K, H), dtype=y_dtype or x.dtype, device=dev)
+    need = grouped_ffn_control_workspace_bytes(T, K, H, F, E_local, w_dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _check(_LIB.moe_grouped_ffn_control(_ptr(x), _dt(x), T, K, H, F, E_local, _ptr(w1), _ptr(w1_scale), _ptr(w2),
+                                        _ptr(w2_scale), w_dt, _ptr(counts), _ptr(offsets), _ptr(row_to_slot),
+                                        _ptr(y), _dt(y), _ptr(workspace), workspace.numel(), _stream(stream, dev)),
+           "moe_grouped_ffn_control")
     return y
 
 

@@ -29,6 +29,9 @@ SIGNATURES = {
     "moe_grouped_ffn": (_int, [_p, _int, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _int, _p, _p, _p, _p, _int,
                                _p, _sz, _p]),
     "moe_grouped_ffn_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32, _int]),
+    "moe_grouped_ffn_control": (_int, [_p, _int, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _int, _p, _p, _p, _p,
+                                       _int, _p, _sz, _p]),
+    "moe_grouped_ffn_control_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32, _int]),
     "moe_combine": (_int, [_p, _int, _p, _p, _i64, _i32, _i32, _p, _int, _p]),
     "moe_pack_ffn_weights": (_int, [_p, _p, _i32, _i32, _i32, _p, _p, _p]),
     "moe_status_string": (ctypes.c_char_p, [_int]),

@@ -164,17 +164,13 @@ __device__ __forceinline__ void load_w_slice(const void* __restrict__ w, const u
 
 // GEMM1 + silu_and_mul.  x [T,H] bf16; w1 [El, 2F, H] (bf16 or MXFP4);
 // act [N, F] bf16 (grouped rows).  KS: K step (128, or 32 when H % 128 != 0).
+// One wave: act columns [n0, n0+16) of the rows [row0, row0+nrows) (nrows <=
+// 16*MB) of expert e.
 template <int MB, int KS, bool MX>
-__global__ __launch_bounds__(kThreads) void ffn1_stream_kernel(
-    const uint16_t* __restrict__ x, int K, int H, int F, int El, const void* __restrict__ w1,
-    const uint8_t* __restrict__ w1s, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ r2s, uint16_t* __restrict__ act) {
-  constexpr int BM = 16 * MB;
-  int e, row0, nrows;
-  if (!find_tile(counts, offsets, El, BM, blockIdx.x, e, row0, nrows)) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n0 = (blockIdx.y * kWaves + wave) * 16;
-  if (n0 >= F) return;
+__device__ __forceinline__ void gemm1_cols(const uint16_t* __restrict__ x, int K, int H, int F,
+                                           const void* __restrict__ w1, const uint8_t* __restrict__ w1s,
+                                           const int32_t* __restrict__ r2s, uint16_t* __restrict__ act, int e,
+                                           int row0, int nrows, int n0, int lane) {
   const int kq = (lane >> 4) * (KS / 4);
 
   const uint16_t* xrow[MB];
@@ -229,18 +225,26 @@ __global__ __launch_bounds__(kThreads) void ffn1_stream_kernel(
   }
 }
 
-// GEMM2.  act [N, F] bf16; w2 [El, H, F]; y [N, H] (bf16 bits or f32).
-template <int MB, int KS, bool MX, typename YT>
-__global__ __launch_bounds__(kThreads) void ffn2_stream_kernel(
-    const uint16_t* __restrict__ act, int H, int F, int El, const void* __restrict__ w2,
-    const uint8_t* __restrict__ w2s, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-    YT* __restrict__ y) {
+template <int MB, int KS, bool MX>
+__global__ __launch_bounds__(kThreads) void ffn1_stream_kernel(
+    const uint16_t* __restrict__ x, int K, int H, int F, int El, const void* __restrict__ w1,
+    const uint8_t* __restrict__ w1s, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ r2s, uint16_t* __restrict__ act) {
   constexpr int BM = 16 * MB;
   int e, row0, nrows;
   if (!find_tile(counts, offsets, El, BM, blockIdx.x, e, row0, nrows)) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n0 = (blockIdx.y * kWaves + wave) * 16;
-  if (n0 >= H) return;
+  if (n0 >= F) return;
+  gemm1_cols<MB, KS, MX>(x, K, H, F, w1, w1s, r2s, act, e, row0, nrows, n0, lane);
+}
+
+// GEMM2.  act [N, F] bf16; w2 [El, H, F]; y [N, H] (bf16 bits or f32).
+// One wave: output columns [n0, n0+16) of the rows [row0, row0+nrows) of expert e.
+template <int MB, int KS, bool MX, typename YT>
+__device__ __forceinline__ void gemm2_cols(const uint16_t* __restrict__ act, int H, int F,
+                                           const void* __restrict__ w2, const uint8_t* __restrict__ w2s,
+                                           YT* __restrict__ y, int e, int row0, int nrows, int n0, int lane) {
   const int kq = (lane >> 4) * (KS / 4);
 
   const uint16_t* arow[MB];
@@ -286,6 +290,98 @@ __global__ __launch_bounds__(kThreads) void ffn2_stream_kernel(
       }
     }
   }
+}
+
+template <int MB, int KS, bool MX, typename YT>
+__global__ __launch_bounds__(kThreads) void ffn2_stream_kernel(
+    const uint16_t* __restrict__ act, int H, int F, int El, const void* __restrict__ w2,
+    const uint8_t* __restrict__ w2s, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    YT* __restrict__ y) {
+  constexpr int BM = 16 * MB;
+  int e, row0, nrows;
+  if (!find_tile(counts, offsets, El, BM, blockIdx.x, e, row0, nrows)) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n0 = (blockIdx.y * kWaves + wave) * 16;
+  if (n0 >= H) return;
+  gemm2_cols<MB, KS, MX, YT>(act, H, F, w2, w2s, y, e, row0, nrows, n0, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Generic persistent scheduler, kept as the A/B control of the b70 lab note
+// "MTP1 M2 compact scheduler closure" (the generic path it measures against:
+// a persistent grouped GEMM that scans every local expert and takes work from
+// a global atomic counter, at a pinned 64-column N tile).  Work item i is
+// (local expert i / NT, N tile i % NT) for every local expert, routed or
+// not; a block claims items from *work until none are left and skips
+// experts without rows.  Results equal the other paths' within rounding (the
+// same sums per output, K walked in the same order).
+
+constexpr int kControlGrid = 256;  // persistent blocks: one per compute unit
+
+__global__ void zero_counters_kernel(int32_t* __restrict__ w) { w[threadIdx.x] = 0; }
+
+template <int KS, bool MX>
+__global__ __launch_bounds__(kThreads) void ffn1_control_kernel(
+    const uint16_t* __restrict__ x, int K, int H, int F, int El, const void* __restrict__ w1,
+    const uint8_t* __restrict__ w1s, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ r2s, uint16_t* __restrict__ act, int32_t* __restrict__ work) {
+  __shared__ int item;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int NT = F / 64, total = El * NT;
+  while (true) {
+    if (threadIdx.x == 0) item = atomicAdd(work, 1);
+    __syncthreads();
+    const int it = item;
+    __syncthreads();
+    if (it >= total) break;
+    const int e = it / NT, n0 = (it % NT) * 64 + wave * 16;
+    const int cnt = counts[e];
+    const int base = offsets[e];
+    for (int m0 = 0; m0 < cnt; m0 += 16)
+      gemm1_cols<1, KS, MX>(x, K, H, F, w1, w1s, r2s, act, e, base + m0, min(16, cnt - m0), n0, lane);
+  }
+}
+
+template <int KS, bool MX, typename YT>
+__global__ __launch_bounds__(kThreads) void ffn2_control_kernel(
+    const uint16_t* __restrict__ act, int H, int F, int El, const void* __restrict__ w2,
+    const uint8_t* __restrict__ w2s, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    YT* __restrict__ y, int32_t* __restrict__ work) {
+  __shared__ int item;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int NT = H / 64, total = El * NT;
+  while (true) {
+    if (threadIdx.x == 0) item = atomicAdd(work, 1);
+    __syncthreads();
+    const int it = item;
+    __syncthreads();
+    if (it >= total) break;
+    const int e = it / NT, n0 = (it % NT) * 64 + wave * 16;
+    const int cnt = counts[e];
+    const int base = offsets[e];
+    for (int m0 = 0; m0 < cnt; m0 += 16)
+      gemm2_cols<1, KS, MX, YT>(act, H, F, w2, w2s, y, e, base + m0, min(16, cnt - m0), n0, lane);
+  }
+}
+
+template <int KS, bool MX>
+hipError_t launch_control_k(const uint16_t* x, int K, int H, int F, int El, const void* w1, const uint8_t* w1s,
+                            const void* w2, const uint8_t* w2s, const int32_t* counts, const int32_t* offsets,
+                            const int32_t* r2s, void* y, int y_dtype, uint16_t* act, int32_t* work,
+                            hipStream_t stream) {
+  hipLaunchKernelGGL(zero_counters_kernel, dim3(1), dim3(2), 0, stream, work);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((ffn1_control_kernel<KS, MX>), dim3(kControlGrid), dim3(kThreads), 0, stream, x, K, H, F, El, w1, w1s,
+                     counts, offsets, r2s, act, work);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (y_dtype == MOE_BF16)
+    hipLaunchKernelGGL((ffn2_control_kernel<KS, MX, uint16_t>), dim3(kControlGrid), dim3(kThreads), 0, stream, act, H, F,
+                       El, w2, w2s, counts, offsets, static_cast<uint16_t*>(y), work + 1);
+  else
+    hipLaunchKernelGGL((ffn2_control_kernel<KS, MX, float>), dim3(kControlGrid), dim3(kThreads), 0, stream, act, H, F, El,
+                       w2, w2s, counts, offsets, static_cast<float*>(y), work + 1);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -675,6 +771,31 @@ hipError_t launch_grouped_ffn(const void* x, int x_dtype, int64_t T, int K, int 
     return dispatch_stream<true>(xb, N, K, H, F, El, w1, w1s, w2, w2s, counts, offsets, r2s, y, y_dtype, act, stream);
   return dispatch_stream<false>(xb, N, K, H, F, El, w1, nullptr, w2, nullptr, counts, offsets, r2s, y, y_dtype, act,
                                 stream);
+}
+
+hipError_t launch_grouped_ffn_control(const void* x, int64_t T, int K, int H, int F, int El, const void* w1,
+                                      const uint8_t* w1s, const void* w2, const uint8_t* w2s, int w_dtype,
+                                      const int32_t* counts, const int32_t* offsets, const int32_t* r2s, void* y,
+                                      int y_dtype, void* workspace, hipStream_t stream) {
+  const int64_t N = T * K;
+  uint16_t* act = static_cast<uint16_t*>(workspace);
+  int32_t* work = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) +
+                                             (grouped_ffn_workspace_bytes(N, H, F, El, w_dtype) + 255) / 256 * 256);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const bool k128 = (H % 128 == 0) && (F % 128 == 0);
+  if (w_dtype == MOE_MXFP4)
+    return k128 ? launch_control_k<128, true>(xb, K, H, F, El, w1, w1s, w2, w2s, counts, offsets, r2s, y, y_dtype, act,
+                                              work, stream)
+                : launch_control_k<32, true>(xb, K, H, F, El, w1, w1s, w2, w2s, counts, offsets, r2s, y, y_dtype, act,
+                                             work, stream);
+  return k128 ? launch_control_k<128, false>(xb, K, H, F, El, w1, nullptr, w2, nullptr, counts, offsets, r2s, y,
+                                             y_dtype, act, work, stream)
+              : launch_control_k<32, false>(xb, K, H, F, El, w1, nullptr, w2, nullptr, counts, offsets, r2s, y,
+                                            y_dtype, act, work, stream);
+}
+
+size_t grouped_ffn_control_workspace_bytes(int64_t N, int H, int F, int El, int w_dtype) {
+  return (grouped_ffn_workspace_bytes(N, H, F, El, w_dtype) + 255) / 256 * 256 + 256;
 }
 
 }  // namespace moe

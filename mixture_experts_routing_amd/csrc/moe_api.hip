@@ -146,6 +146,35 @@ int moe_grouped_ffn(const void* x, int x_dtype, int64_t T, int32_t K, int32_t H,
                                             static_cast<hipStream_t>(stream)));
 }
 
+size_t moe_grouped_ffn_control_workspace_bytes(int64_t T, int32_t K, int32_t H, int32_t F, int32_t E_local,
+                                               int w_dtype) {
+  if (T <= 0 || K <= 0 || F <= 0 || H <= 0 || E_local <= 0) return 0;
+  return moe::grouped_ffn_control_workspace_bytes(T * K, H, F, E_local, w_dtype);
+}
+
+int moe_grouped_ffn_control(const void* x, int x_dtype, int64_t T, int32_t K, int32_t H, int32_t F,
+                            int32_t E_local, const void* w1, const uint8_t* w1_scale, const void* w2,
+                            const uint8_t* w2_scale, int w_dtype, const int32_t* counts, const int32_t* offsets,
+                            const int32_t* row_to_slot, void* y, int y_dtype, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (T < 0 || K < 1 || H < 1 || F < 1 || E_local < 1) return MOE_ERR_INVALID_ARG;
+  if (y_dtype != MOE_F32 && y_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (x_dtype != MOE_BF16 || (w_dtype != MOE_BF16 && w_dtype != MOE_MXFP4)) return MOE_ERR_UNSUPPORTED;
+  if (H % 64 != 0 || F % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (T * (int64_t)K >= ((int64_t)1 << 31) || (int64_t)E_local * (H > F ? H : F) / 64 >= ((int64_t)1 << 31))
+    return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !w1 || !w2 || !counts || !offsets || !row_to_slot || !y) return MOE_ERR_INVALID_ARG;
+  if (w_dtype == MOE_MXFP4 && (!w1_scale || !w2_scale)) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe::grouped_ffn_control_workspace_bytes(T * K, H, F, E_local, w_dtype);
+  if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_grouped_ffn_control(x, T, K, H, F, E_local, w1, w1_scale, w2, w2_scale, w_dtype,
+                                                    counts, offsets, row_to_slot, y, y_dtype, workspace,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
 int moe_pack_ffn_weights(const void* w1, const void* w2, int32_t E_local, int32_t H, int32_t F, void* w1_tiled,
                          void* w2_tiled, void* stream) {
   if (E_local < 1 || H < 1 || F < 1) return MOE_ERR_INVALID_ARG;

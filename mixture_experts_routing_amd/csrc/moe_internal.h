@@ -158,6 +158,14 @@ __host__ __device__ constexpr int panel_w1_row(int R, int nt, int F) {
 // W2 row held by row R of GEMM2 panel nt
 __host__ __device__ constexpr int panel_w2_row(int R, int nt) { return nt * kPanelRows + R; }
 
+// generic persistent scheduler (atomic work counter over every local expert,
+// 64-column N tiles), the A/B control of the compact one
+size_t grouped_ffn_control_workspace_bytes(int64_t N, int H, int F, int El, int w_dtype);
+hipError_t launch_grouped_ffn_control(const void* x, int64_t T, int K, int H, int F, int El, const void* w1,
+                                      const uint8_t* w1s, const void* w2, const uint8_t* w2s, int w_dtype,
+                                      const int32_t* counts, const int32_t* offsets, const int32_t* r2s, void* y,
+                                      int y_dtype, void* workspace, hipStream_t stream);
+
 // LDS-tiled MFMA path for many rows per expert (bf16 weights, row-major or
 // tile-packed)
 bool tiled_ffn_applicable(int64_t N, int H, int F, int El);
