@@ -352,13 +352,26 @@ def bench_decode(dev, reps):
 
         t_a, t_b = ab_graph_ms(each(compact, ffn, combine), each(compact, ffn_control, combine), reps, dev)
         t_a, t_b = t_a / nvar, t_b / nvar
+        # boundary fusion: compaction and combine inside the two FFN kernels,
+        # A/B against the three separate calls (alternated replays)
+        xws = torch.empty(moe.fused_experts_workspace_bytes(T, K, H, F, El, moe.MOE_BF16), dtype=torch.uint8,
+                          device=dev)
+
+        def fused(v):
+            moe.moe_fused_experts(x, variants[v], tw, w1, w2, emap_d, Eg, out=out, routes=outs[v], workspace=xws)
+
+        t_sep, t_fus = ab_graph_ms(each(compact, ffn, combine), each(fused), reps, dev)
+        t_sep, t_fus = t_sep / nvar, t_fus / nvar
         n_exp = len({l for r in synth.DECODE_PATTERNS[pat] for l in r if l is not None})
         wbytes = n_exp * (2 * F * H + H * F) * 2
         d = {"layer_ms": round(t_layer, 4), "compact_ms": round(t_cmp, 4), "ffn_ms": round(t_ffn, 4),
              "combine_ms": round(t_cmb, 4), "tokens_per_s": round(T / (t_layer / 1e3), 1),
              "local_experts": n_exp, "weight_bytes": wbytes,
              "ab_layer_ms": {"compact": round(t_a, 4), "generic_control": round(t_b, 4)},
-             "projected_saved_ms_43_layers": round((t_b - t_a) * 43, 4)}
+             "projected_saved_ms_43_layers": round((t_b - t_a) * 43, 4),
+             "boundary_fusion": {"upper_bound_saved_ms_43_layers": round((t_layer - t_ffn) * 43, 4),
+                                 "ab_layer_ms": {"separate": round(t_sep, 4), "fused": round(t_fus, 4)},
+                                 "saved_ms_43_layers": round((t_sep - t_fus) * 43, 4)}}
         if wbytes:
             gbs = wbytes / (t_ffn / 1e3) / 1e9
             d.update({"ffn_weight_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
@@ -367,10 +380,14 @@ def bench_decode(dev, reps):
     nonempty = [p for p in res if res[p]["local_experts"] > 0]
     worst = min(nonempty, key=lambda p: res[p]["hbm_frac"])
     saved = {p: res[p]["projected_saved_ms_43_layers"] for p in res}
+    fsaved = {p: res[p]["boundary_fusion"]["saved_ms_43_layers"] for p in res}
     return {"patterns": res, "min_hbm_frac_pattern": worst, "min_hbm_frac": res[worst]["hbm_frac"],
             "min_tokens_per_s": min(res[p]["tokens_per_s"] for p in res),
             "scheduler_ab": {"min_projected_saved_ms_43_layers": min(saved.values()),
-                             "min_pattern": min(saved, key=saved.get)}}
+                             "min_pattern": min(saved, key=saved.get)},
+            "boundary_fusion": {"min_saved_ms_43_layers": min(fsaved.values()), "min_pattern": min(fsaved, key=fsaved.get),
+                                "min_upper_bound_ms_43_layers": min(
+                                    res[p]["boundary_fusion"]["upper_bound_saved_ms_43_layers"] for p in res)}}
 
 
 # ---------------------------------------------------------------------------

@@ -208,6 +208,43 @@ size_t moe_grouped_ffn_control_workspace_bytes(int64_t T, int32_t K, int32_t H, 
                                                int32_t E_local, int w_dtype);
 
 /*
+ * moe_fused_experts -- the layer after the gate for decode batches, with the
+ * remap and final-gather boundaries removed: route compaction, grouped SwiGLU
+ * FFN and top-k weighted combine in two kernel launches.
+ * Source: b70 lab note "MTP1 M2 compact scheduler closure", closing paragraph
+ * (next screen: remove the remap and the final permuted gather while keeping
+ * compact scheduling and the grouped weight reuse).
+ *
+ * Computes exactly what moe_route_compact, then moe_grouped_ffn (y in bf16),
+ * then moe_combine compute on the same inputs, with the grouped y rows never
+ * stored: the first kernel derives the compaction itself from topk_ids and
+ * expert_map (and stores it in counts/offsets/slot_to_row/row_to_slot, which
+ * are bit-identical to moe_route_compact's), the second adds each token's
+ * weighted rows, in ascending k, as soon as its columns are computed.  The
+ * reduction of the second GEMM may be split differently from moe_grouped_ffn,
+ * so out agrees with the three-call path within rounding (bit-identical when
+ * all local rows fall in one 16-row tile).
+ *   x [T, H] bf16; topk_ids, topk_weights [T, K]; expert_map as for
+ *   moe_route_compact; w1, w2 (+ scales) as for moe_grouped_ffn with w_dtype
+ *   MOE_BF16 or MOE_MXFP4; counts [E_local], offsets [E_local+1],
+ *   slot_to_row [T*K], row_to_slot [T*K]: outputs as for moe_route_compact;
+ *   out [T, H] (out_dtype MOE_BF16 or MOE_F32): partial sum over local routes.
+ * workspace: moe_fused_experts_workspace_bytes(...) bytes (the act rows),
+ * 16-byte aligned.
+ * Limits: T*K <= 64, E_local <= 64, H % 32 == 0, F % 32 == 0
+ * (MOE_ERR_UNSUPPORTED otherwise: larger batches take the separate calls).
+ * T == 0 writes counts = 0 and offsets = 0 and nothing else.
+ */
+int moe_fused_experts(const void* x, int x_dtype, int64_t T, int32_t K, int32_t H, int32_t F,
+                      const int32_t* topk_ids, const float* topk_weights, const int32_t* expert_map, int32_t E_global,
+                      int32_t E_local, const void* w1, const uint8_t* w1_scale, const void* w2,
+                      const uint8_t* w2_scale, int w_dtype, int32_t* counts, int32_t* offsets, int32_t* slot_to_row,
+                      int32_t* row_to_slot, void* out, int out_dtype, void* workspace, size_t workspace_bytes,
+                      void* stream);
+size_t moe_fused_experts_workspace_bytes(int64_t T, int32_t K, int32_t H, int32_t F, int32_t E_local,
+                                         int w_dtype);
+
+/*
  * moe_pack_ffn_weights -- store bf16 expert weights in the tile-packed layout
  * (MOE_BF16_TILED) that the many-rows-per-expert FFN kernels stream with
  * contiguous loads.  A one-time transform of the weights (model load), not

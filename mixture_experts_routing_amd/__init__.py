@@ -18,8 +18,9 @@ from ._lib import MOE_BF16, MOE_BF16_TILED, MOE_F32, MOE_MXFP4
 _LIB = _lib.load()
 
 __all__ = [
-    "moe_topk_softmax", "moe_route_compact", "moe_grouped_ffn", "moe_combine", "moe_layer",
-    "MOE_F32", "MOE_BF16", "MOE_MXFP4", "MOE_BF16_TILED", "moe_pack_ffn_weights", "moe_topk_sigmoid", "moe_route_align", "moe_grouped_ffn_control", "MoeError", "library_path",
+    "moe_topk_softmax", "moe_topk_sigmoid", "moe_route_compact", "moe_route_align", "moe_grouped_ffn",
+    "moe_grouped_ffn_control", "moe_fused_experts", "moe_combine", "moe_pack_ffn_weights", "moe_layer",
+    "MOE_F32", "MOE_BF16", "MOE_MXFP4", "MOE_BF16_TILED", "MoeError", "library_path",
 ]
 
 
@@ -260,6 +261,48 @@ def moe_combine(y: torch.Tensor, topk_weights: torch.Tensor, slot_to_row: torch.
     _check(_LIB.moe_combine(_ptr(y), _dt(y), _ptr(topk_weights), _ptr(slot_to_row), T, K, H, _ptr(out), _dt(out),
                             _stream(stream, dev)), "moe_combine")
     return out
+
+
+def fused_experts_workspace_bytes(T: int, K: int, H: int, F: int, E_local: int, w_dtype: int) -> int:
+    return int(_LIB.moe_fused_experts_workspace_bytes(T, K, H, F, E_local, w_dtype))
+
+
+def moe_fused_experts(x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor, w1: torch.Tensor,
+                      w2: torch.Tensor, expert_map: Optional[torch.Tensor] = None, E_global: Optional[int] = None,
+                      w1_scale: Optional[torch.Tensor] = None, w2_scale: Optional[torch.Tensor] = None,
+                      out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None, routes=None,
+                      workspace: Optional[torch.Tensor] = None, stream=None):
+    """Decode batches (T*K <= 64, E_local <= 64): compaction, grouped FFN and
+    combine in two launches.  x [T, H] bf16, topk_ids / topk_weights [T, K],
+    weights as for moe_grouped_ffn (bf16 or MXFP4).
+    Returns (out [T, H], (counts, offsets, slot_to_row, row_to_slot))."""
+    dev = _dev(x, topk_ids, topk_weights, w1, w2, expert_map, w1_scale, w2_scale)
+    T, H = x.shape
+    K = topk_ids.shape[1]
+    E_local = w1.shape[0]
+    if E_global is None:
+        E_global = expert_map.numel() if expert_map is not None else E_local
+    if w1.dtype == torch.uint8:
+        w_dt, F = MOE_MXFP4, w2.shape[2] * 2
+    else:
+        w_dt, F = _dt(w1), w2.shape[2]
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype or x.dtype, device=dev)
+    if routes is None:
+        routes = (torch.empty(E_local, dtype=torch.int32, device=dev),
+                  torch.empty(E_local + 1, dtype=torch.int32, device=dev),
+                  torch.empty(T * K, dtype=torch.int32, device=dev),
+                  torch.empty(T * K, dtype=torch.int32, device=dev))
+    counts, offsets, s2r, r2s = routes
+    need = fused_experts_workspace_bytes(T, K, H, F, E_local, w_dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _check(_LIB.moe_fused_experts(_ptr(x), _dt(x), T, K, H, F, _ptr(topk_ids), _ptr(topk_weights),
+                                  _ptr(expert_map), E_global, E_local, _ptr(w1), _ptr(w1_scale), _ptr(w2),
+                                  _ptr(w2_scale), w_dt, _ptr(counts), _ptr(offsets), _ptr(s2r), _ptr(r2s),
+                                  _ptr(out), _dt(out), _ptr(workspace), workspace.numel(), _stream(stream, dev)),
+           "moe_fused_experts")
+    return out, routes
 
 
 def moe_layer(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, K: int, logits: Optional[torch.Tensor] = None,

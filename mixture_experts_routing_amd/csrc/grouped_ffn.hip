@@ -85,12 +85,12 @@ struct TileTab {
   int cnt, off, nt, incl, total;
 };
 
-__device__ __forceinline__ TileTab load_tile_tab(const int32_t* __restrict__ counts,
-                                                 const int32_t* __restrict__ offsets, int El, int BM) {
+// From each lane's own expert count and first row (lanes >= El: count 0).
+__device__ __forceinline__ TileTab make_tile_tab(int cnt, int off, int BM) {
   const int lane = threadIdx.x & 63;
   TileTab t;
-  t.cnt = lane < El ? counts[lane] : 0;
-  t.off = lane < El ? offsets[lane] : 0;
+  t.cnt = cnt;
+  t.off = off;
   t.nt = (t.cnt + BM - 1) / BM;
   int inc = t.nt;
 #pragma unroll
@@ -101,6 +101,49 @@ __device__ __forceinline__ TileTab load_tile_tab(const int32_t* __restrict__ cou
   t.incl = inc;
   t.total = __shfl(inc, 63, 64);
   return t;
+}
+
+__device__ __forceinline__ TileTab load_tile_tab(const int32_t* __restrict__ counts,
+                                                 const int32_t* __restrict__ offsets, int El, int BM) {
+  const int lane = threadIdx.x & 63;
+  return make_tile_tab(lane < El ? counts[lane] : 0, lane < El ? offsets[lane] : 0, BM);
+}
+
+// Route compaction of at most 64 slots (one per lane) into at most 64 local
+// experts, in one wave's registers -- the same stable counting sort as the
+// one-wave compaction kernel: the row of slot s is the number of local slots
+// with a smaller local id plus the number of earlier slots with the same id.
+// Lane e also gets expert e's count and first row; lane r gets the slot of
+// row r (-1 for r >= R).  N, Eg, El are wave-uniform.
+struct WaveRoutes {
+  int row;  // this lane's slot: its grouped row, -1 if remote or lane >= N
+  int cnt;  // expert `lane`: routed rows
+  int off;  // expert `lane`: first row (R for lanes >= El)
+  int inv;  // row `lane`: its slot, -1 if lane >= R
+  int R;    // local rows (uniform)
+};
+
+__device__ __forceinline__ WaveRoutes wave_routes(const int32_t* __restrict__ ids, int N,
+                                                 const int32_t* __restrict__ emap, int Eg, int El) {
+  const int lane = threadIdx.x & 63;
+  const int l = lane < N ? local_expert(ids[lane], emap, Eg, El) : -1;
+  WaveRoutes w;
+  int row = 0, cnt = 0, off = 0;
+  for (int j = 0; j < N; ++j) {
+    const int lj = __builtin_amdgcn_readlane(l, j);
+    const bool ok = lj >= 0;
+    cnt += (lj == lane) ? 1 : 0;
+    off += (ok && lj < lane) ? 1 : 0;
+    row += (ok && (lj < l || (lj == l && j < lane))) ? 1 : 0;
+  }
+  w.row = l >= 0 ? row : -1;
+  w.cnt = cnt;
+  w.off = off;
+  w.R = __popcll(__ballot(l >= 0));
+  int inv = -1;
+  for (int j = 0; j < N; ++j) inv = (__builtin_amdgcn_readlane(w.row, j) == lane) ? j : inv;
+  w.inv = inv;
+  return w;
 }
 
 // Tile i (< t.total): expert, first grouped row, valid rows (wave-uniform).
@@ -462,19 +505,51 @@ struct WUnit<true> {
   __device__ __forceinline__ bf16x8 get() const { return widen_mx8(c, e8); }
 };
 
+// Compaction inputs and outputs of the fused GEMM1 (ROUTES = true): every
+// wave derives the route table itself from topk_ids and the expert map, and
+// block 0 stores it for the kernels that follow and for the caller.
+struct FusedRoutes {
+  const int32_t* ids;
+  const int32_t* emap;
+  int N, Eg;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* s2r;
+  int32_t* r2s;
+};
+
 // GEMM1 + silu_and_mul for the decode regime.  Same operands as
-// ffn1_stream_kernel.
-template <bool MX>
+// ffn1_stream_kernel; with ROUTES, counts/offsets/r2s are unused and the
+// route table comes from `fr` (El <= 64, N <= 64).
+template <bool MX, bool ROUTES>
 __global__ __launch_bounds__(kDecThreads) void ffn1_decode_kernel(
     const uint16_t* __restrict__ x, int K, int H, int F, int El, const void* __restrict__ w1,
     const uint8_t* __restrict__ w1s, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ r2s, uint16_t* __restrict__ act) {
+    const int32_t* __restrict__ r2s, uint16_t* __restrict__ act, FusedRoutes fr) {
   constexpr int U = dec_unroll1<MX>();
   __shared__ float red[kDecWaves][8][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
-  const bool small = El <= 64;  // uniform
+  const bool small = ROUTES || El <= 64;  // uniform
   TileTab tab{};
-  if (small) tab = load_tile_tab(counts, offsets, El, 16);
+  int inv = -1;  // ROUTES: slot of row `lane`
+  if constexpr (ROUTES) {
+    const WaveRoutes wr = wave_routes(fr.ids, fr.N, fr.emap, fr.Eg, El);
+    tab = make_tile_tab(wr.cnt, wr.off, 16);
+    inv = wr.inv;
+    if (blockIdx.x == 0 && wave == 0) {
+      if (lane < El) {
+        fr.counts[lane] = wr.cnt;
+        fr.offsets[lane] = wr.off;
+      }
+      if (lane == 0) fr.offsets[El] = wr.R;
+      if (lane < fr.N) {
+        fr.s2r[lane] = wr.row;
+        fr.r2s[lane] = wr.inv;
+      }
+    }
+  } else if (small) {
+    tab = load_tile_tab(counts, offsets, El, 16);
+  }
   const int tiles = small ? tab.total : count_tiles(counts, El, 16);
   const int CG = F / 16, units = H / 32;
   const int S = decode_split(tiles, CG, units);
@@ -495,7 +570,11 @@ __global__ __launch_bounds__(kDecThreads) void ffn1_decode_kernel(
     f32x4 ag = {0, 0, 0, 0}, au = {0, 0, 0, 0};
     if (active) {
       // rows past the tile's end reuse the first row; their results are dropped
-      const int tok = r2s[row0 + (c < nrows ? c : 0)] / K;
+      const int r = row0 + (c < nrows ? c : 0);
+      int slot;
+      if constexpr (ROUTES) slot = __shfl(inv, r, 64);
+      else slot = r2s[r];
+      const int tok = slot / K;
       const uint16_t* xr = x + (int64_t)tok * H;
       const int64_t rg = (int64_t)e * 2 * F + cg * 16 + c, ru = rg + F;
       int u = u_begin;
@@ -632,8 +711,8 @@ template <bool MX>
 hipError_t launch_decode(const uint16_t* x, int K, int H, int F, int El, const void* w1, const uint8_t* w1s,
                          const void* w2, const uint8_t* w2s, const int32_t* counts, const int32_t* offsets,
                          const int32_t* r2s, void* y, int y_dtype, uint16_t* act, hipStream_t stream) {
-  hipLaunchKernelGGL((ffn1_decode_kernel<MX>), dim3(kDecGrid), dim3(kDecThreads), 0, stream, x, K, H, F, El, w1, w1s,
-                     counts, offsets, r2s, act);
+  hipLaunchKernelGGL((ffn1_decode_kernel<MX, false>), dim3(kDecGrid), dim3(kDecThreads), 0, stream, x, K, H, F, El,
+                     w1, w1s, counts, offsets, r2s, act, FusedRoutes{});
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (y_dtype == MOE_BF16)
@@ -642,6 +721,116 @@ hipError_t launch_decode(const uint16_t* x, int K, int H, int F, int El, const v
   else
     hipLaunchKernelGGL((ffn2_decode_kernel<MX, float>), dim3(kDecGrid), dim3(kDecThreads), 0, stream, act, H, F, El,
                        w2, w2s, counts, offsets, static_cast<float*>(y));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Boundary fusion for decode batches (N = T*K <= kFusedMaxSlots slots, at
+// most 64 local experts): the route compaction runs in the prologue of the
+// GEMM1 kernel (ffn1_decode_kernel<MX, true>) and the combine in the tail of
+// the GEMM2 kernel below, so the layer after the gate is two launches.
+
+// GEMM2 with the combine in its tail.  Block b owns the 16 output columns
+// [16 cg, 16 cg + 16), cg = b, b + grid, ..., across every tile: the 16 waves
+// split the reduction 16 ways for one tile at a time, wave 0 adds the
+// partials in split order and keeps the tile's y values, rounded to bf16, in
+// LDS.  When all tiles are done the block forms
+//   out[t, cols] = sum over k ascending, slot local, of w[t,k] * y[row, cols]
+// from LDS -- the combine kernel's arithmetic -- so y never goes to memory.
+template <bool MX, typename OT>
+__global__ __launch_bounds__(kDecThreads) void ffn2_combine_kernel(
+    const uint16_t* __restrict__ act, int H, int F, int El, const void* __restrict__ w2,
+    const uint8_t* __restrict__ w2s, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ s2r, const float* __restrict__ tw, int T, int K, OT* __restrict__ out) {
+  __shared__ float red[kDecWaves][4][64];
+  __shared__ float ys[kFusedMaxSlots][16];  // y[row, 16 cg + col]
+  __shared__ int srow[kFusedMaxSlots];
+  __shared__ float sw[kFusedMaxSlots];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  const int N = T * K;
+  if ((int)threadIdx.x < N) {
+    srow[threadIdx.x] = s2r[threadIdx.x];
+    sw[threadIdx.x] = tw[threadIdx.x];
+  }
+  const TileTab tab = load_tile_tab(counts, offsets, El, 16);
+  const int tiles = tab.total;
+  const int CG = H / 16, units = F / 32;
+  const int per = (units + kDecWaves - 1) / kDecWaves;
+  const int u_begin = min(units, wave * per), u_end = min(units, u_begin + per);
+  __syncthreads();  // srow, sw
+
+  for (int cg = blockIdx.x; cg < CG; cg += gridDim.x) {
+    for (int tile = 0; tile < tiles; ++tile) {
+      int e = 0, row0 = 0, nrows = 0;
+      tab_find(tab, 16, tile, e, row0, nrows);
+      f32x4 acc = {0, 0, 0, 0};
+      const uint16_t* ar = act + (int64_t)(row0 + (c < nrows ? c : 0)) * F;
+      const int64_t rw = (int64_t)e * H + cg * 16 + c;
+      int u = u_begin;
+      for (; u + kDecUnroll <= u_end; u += kDecUnroll) {
+        WUnit<MX> b[kDecUnroll];
+        bf16x8 a[kDecUnroll];
+#pragma unroll
+        for (int j = 0; j < kDecUnroll; ++j) b[j].load(w2, w2s, rw, F, u + j, g);
+#pragma unroll
+        for (int j = 0; j < kDecUnroll; ++j) a[j] = unit_bf16(ar, u + j, g);
+#pragma unroll
+        for (int j = 0; j < kDecUnroll; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], b[j].get(), acc, 0, 0, 0);
+      }
+      for (; u < u_end; ++u) {
+        WUnit<MX> b;
+        b.load(w2, w2s, rw, F, u, g);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unit_bf16(ar, u, g), b.get(), acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave][i][lane] = acc[i];
+      __syncthreads();
+      if (wave == 0) {
+        for (int sp = 1; sp < kDecWaves; ++sp) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] += red[sp][i][lane];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = g * 4 + i;
+          if (m < nrows) ys[row0 + m][c] = bf16_bits_to_f32(f32_to_bf16_bits(acc[i]));
+        }
+      }
+      __syncthreads();  // red is rewritten by the next tile; ys complete
+    }
+    for (int i = threadIdx.x; i < T * 16; i += kDecThreads) {
+      const int t = i >> 4, col = i & 15;
+      float a = 0.0f;
+      for (int k = 0; k < K; ++k) {
+        const int r = srow[t * K + k];
+        if (r >= 0) a = fmaf(sw[t * K + k], ys[r][col], a);
+      }
+      const int64_t o = (int64_t)t * H + cg * 16 + col;
+      if constexpr (sizeof(OT) == 2) out[o] = f32_to_bf16_bits(a);
+      else out[o] = a;
+    }
+    __syncthreads();  // ys is rewritten for the next column group
+  }
+}
+
+template <bool MX>
+hipError_t launch_fused_k(const uint16_t* x, int64_t T, int K, int H, int F, const int32_t* ids, const float* tw,
+                          const int32_t* emap, int Eg, int El, const void* w1, const uint8_t* w1s, const void* w2,
+                          const uint8_t* w2s, int32_t* counts, int32_t* offsets, int32_t* s2r, int32_t* r2s,
+                          void* out, int out_dtype, uint16_t* act, hipStream_t stream) {
+  const FusedRoutes fr{ids, emap, (int)(T * K), Eg, counts, offsets, s2r, r2s};
+  hipLaunchKernelGGL((ffn1_decode_kernel<MX, true>), dim3(kDecGrid), dim3(kDecThreads), 0, stream, x, K, H, F, El,
+                     w1, w1s, static_cast<const int32_t*>(nullptr), static_cast<const int32_t*>(nullptr),
+                     static_cast<const int32_t*>(nullptr), act, fr);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || T == 0) return err;  // T == 0: counts and offsets (zeros) are written
+  const unsigned grid = (unsigned)min(kDecGrid, H / 16);
+  if (out_dtype == MOE_BF16)
+    hipLaunchKernelGGL((ffn2_combine_kernel<MX, uint16_t>), dim3(grid), dim3(kDecThreads), 0, stream, act, H, F, El,
+                       w2, w2s, counts, offsets, s2r, tw, (int)T, K, static_cast<uint16_t*>(out));
+  else
+    hipLaunchKernelGGL((ffn2_combine_kernel<MX, float>), dim3(grid), dim3(kDecThreads), 0, stream, act, H, F, El,
+                       w2, w2s, counts, offsets, s2r, tw, (int)T, K, static_cast<float*>(out));
   return hipGetLastError();
 }
 
@@ -796,6 +985,21 @@ hipError_t launch_grouped_ffn_control(const void* x, int64_t T, int K, int H, in
 
 size_t grouped_ffn_control_workspace_bytes(int64_t N, int H, int F, int El, int w_dtype) {
   return (grouped_ffn_workspace_bytes(N, H, F, El, w_dtype) + 255) / 256 * 256 + 256;
+}
+
+size_t fused_experts_workspace_bytes(int64_t N, int F) { return (size_t)N * (size_t)F * sizeof(uint16_t); }
+
+hipError_t launch_fused_experts(const uint16_t* x, int64_t T, int K, int H, int F, const int32_t* ids,
+                                const float* topk_weights, const int32_t* emap, int Eg, int El, const void* w1,
+                                const uint8_t* w1s, const void* w2, const uint8_t* w2s, int w_dtype,
+                                int32_t* counts, int32_t* offsets, int32_t* s2r, int32_t* r2s, void* out,
+                                int out_dtype, void* workspace, hipStream_t stream) {
+  uint16_t* act = static_cast<uint16_t*>(workspace);
+  if (w_dtype == MOE_MXFP4)
+    return launch_fused_k<true>(x, T, K, H, F, ids, topk_weights, emap, Eg, El, w1, w1s, w2, w2s, counts, offsets,
+                                s2r, r2s, out, out_dtype, act, stream);
+  return launch_fused_k<false>(x, T, K, H, F, ids, topk_weights, emap, Eg, El, w1, w1s, w2, w2s, counts, offsets,
+                               s2r, r2s, out, out_dtype, act, stream);
 }
 
 }  // namespace moe

@@ -175,6 +175,45 @@ int moe_grouped_ffn_control(const void* x, int x_dtype, int64_t T, int32_t K, in
                                                     static_cast<hipStream_t>(stream)));
 }
 
+size_t moe_fused_experts_workspace_bytes(int64_t T, int32_t K, int32_t H, int32_t F, int32_t E_local,
+                                         int w_dtype) {
+  (void)H;
+  (void)E_local;
+  (void)w_dtype;
+  if (T <= 0 || K <= 0 || F <= 0) return 0;
+  return moe::fused_experts_workspace_bytes(T * K, F);
+}
+
+int moe_fused_experts(const void* x, int x_dtype, int64_t T, int32_t K, int32_t H, int32_t F,
+                      const int32_t* topk_ids, const float* topk_weights, const int32_t* expert_map, int32_t E_global,
+                      int32_t E_local, const void* w1, const uint8_t* w1_scale, const void* w2,
+                      const uint8_t* w2_scale, int w_dtype, int32_t* counts, int32_t* offsets, int32_t* slot_to_row,
+                      int32_t* row_to_slot, void* out, int out_dtype, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (T < 0 || K < 1 || H < 1 || F < 1 || E_local < 1 || E_global < 1 || E_local > E_global)
+    return MOE_ERR_INVALID_ARG;
+  if (!expert_map && E_local != E_global) return MOE_ERR_INVALID_ARG;
+  if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (x_dtype != MOE_BF16 || (w_dtype != MOE_BF16 && w_dtype != MOE_MXFP4)) return MOE_ERR_UNSUPPORTED;
+  if (H % 32 != 0 || F % 32 != 0) return MOE_ERR_UNSUPPORTED;
+  if (T * (int64_t)K > moe::kFusedMaxSlots || E_local > moe::kFusedMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
+  if (T > 0) {
+    if (!x || !topk_ids || !topk_weights || !w1 || !w2 || !slot_to_row || !row_to_slot || !out)
+      return MOE_ERR_INVALID_ARG;
+    if (w_dtype == MOE_MXFP4 && (!w1_scale || !w2_scale)) return MOE_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16)) return MOE_ERR_INVALID_ARG;
+    const size_t need = moe::fused_experts_workspace_bytes(T * K, F);
+    if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return MOE_ERR_INVALID_ARG;
+  }
+  // T == 0 still defines counts = 0 and offsets = 0
+  return hip_status(moe::launch_fused_experts(static_cast<const uint16_t*>(x), T, K, H, F, topk_ids, topk_weights,
+                                              expert_map, E_global, E_local, w1, w1_scale, w2, w2_scale, w_dtype,
+                                              counts, offsets, slot_to_row, row_to_slot, out, out_dtype, workspace,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 int moe_pack_ffn_weights(const void* w1, const void* w2, int32_t E_local, int32_t H, int32_t F, void* w1_tiled,
                          void* w2_tiled, void* stream) {
   if (E_local < 1 || H < 1 || F < 1) return MOE_ERR_INVALID_ARG;

@@ -111,6 +111,15 @@ __device__ __forceinline__ float group_sum_f32(float x) {
   return x;
 }
 
+// Local expert of a global id on this rank: -1 for a remote expert (map
+// value outside [0, El)) and for an id outside [0, Eg).  emap == nullptr is
+// the identity map.
+__device__ __forceinline__ int local_expert(int id, const int32_t* __restrict__ emap, int Eg, int El) {
+  if (id < 0 || id >= Eg) return -1;
+  const int l = emap ? emap[id] : id;
+  return (l >= 0 && l < El) ? l : -1;
+}
+
 // ---------------------------------------------------------------------------
 // host-side launchers (one per kernel family), called after validation
 
@@ -176,6 +185,17 @@ hipError_t launch_tiled_ffn(const uint16_t* x, int64_t T, int64_t N, int topk, i
                             hipStream_t stream);
 hipError_t launch_pack_ffn_weights(const uint16_t* w1, const uint16_t* w2, int El, int H, int F, uint16_t* w1t,
                                    uint16_t* w2t, hipStream_t stream);
+
+// boundary fusion for decode batches: route compaction inside the GEMM1
+// kernel, combine inside the GEMM2 kernel (T*K <= kFusedMaxSlots, El <= 64)
+constexpr int kFusedMaxSlots = 64;
+constexpr int kFusedMaxExperts = 64;
+size_t fused_experts_workspace_bytes(int64_t N, int F);
+hipError_t launch_fused_experts(const uint16_t* x, int64_t T, int K, int H, int F, const int32_t* ids,
+                                const float* topk_weights, const int32_t* emap, int Eg, int El, const void* w1,
+                                const uint8_t* w1s, const void* w2, const uint8_t* w2s, int w_dtype,
+                                int32_t* counts, int32_t* offsets, int32_t* s2r, int32_t* r2s, void* out,
+                                int out_dtype, void* workspace, hipStream_t stream);
 
 hipError_t launch_combine(const void* y, int y_dtype, const float* w, const int32_t* slot_to_row,
                           int64_t T, int K, int H, void* out, int out_dtype, hipStream_t stream);

@@ -35,9 +35,7 @@ constexpr int kSingleMax = kWaves * kGroupsSingle * 64;  // 4096 slots
 constexpr int kBlockSlots = kWaves * 64;               // slots per block, multi-block path
 
 __device__ __forceinline__ int local_of(int id, const int32_t* __restrict__ emap, int Eg, int El) {
-  if (id < 0 || id >= Eg) return -1;
-  const int l = emap ? emap[id] : id;
-  return (l >= 0 && l < El) ? l : -1;
+  return local_expert(id, emap, Eg, El);
 }
 
 // For a group of 64 lanes holding local ids l (-1 = remote/absent): the

@@ -93,3 +93,29 @@ def test_combine_validation(lib):
     assert f(FAKE, 2, FAKE, FAKE, 2, 6, 4096, FAKE, 1, NULL) == 2   # y dtype
     assert f(FAKE, 1, NULL, FAKE, 2, 6, 4096, FAKE, 1, NULL) == 1   # null weights
     assert f(FAKE, 1, FAKE, FAKE, 2, 0, 4096, FAKE, 1, NULL) == 1   # K == 0
+
+
+@_no_gpu
+def test_fused_experts_validation(lib):
+    f = lib.moe_fused_experts
+    def args(T=2, K=6, H=4096, F=2048, El=40, Eg=256, emap=FAKE, xdt=1, wdt=1, odt=1, sc=NULL, ws=FAKE,
+             wsb=1 << 40, counts=FAKE, x=FAKE):
+        return (x, xdt, T, K, H, F, FAKE, FAKE, emap, Eg, El, FAKE, sc, FAKE, sc, wdt, counts, FAKE, FAKE, FAKE,
+                FAKE, odt, ws, wsb, NULL)
+
+    assert f(*args(T=9, K=8)) == 2              # 72 slots: more than one wave's worth
+    assert f(*args(El=65, Eg=256)) == 2         # more than 64 local experts
+    assert f(*args(H=4008)) == 2                # H not a multiple of 32
+    assert f(*args(F=2040)) == 2                # F not a multiple of 32
+    assert f(*args(xdt=0, wdt=0)) == 2          # fp32 pair: not on this path
+    assert f(*args(wdt=3)) == 2                 # tile-packed weights: not on this path
+    assert f(*args(odt=2)) == 2                 # out as MXFP4
+    assert f(*args(wdt=2)) == 1                 # MXFP4 codes without scales
+    assert f(*args(emap=NULL)) == 1             # no map while E_local != E_global
+    assert f(*args(El=40, Eg=32)) == 1          # E_local > E_global
+    assert f(*args(counts=NULL)) == 1           # null counts
+    assert f(*args(ws=NULL)) == 4
+    need = lib.moe_fused_experts_workspace_bytes(2, 6, 4096, 2048, 40, 1)
+    assert need == 2 * 6 * 2048 * 2             # the bf16 act rows
+    assert f(*args(wsb=need - 1)) == 4
+    assert f(*args(x=ctypes.c_void_p(0x1002))) == 1  # x must be 16-byte aligned
