@@ -436,10 +436,10 @@ hipError_t launch_control_k(const uint16_t* x, int K, int H, int F, int El, cons
 // takes an item -- one M-tile and 16/S groups of 16 columns -- and its 16
 // waves split the reduction dimension S ways.  The partial accumulators meet
 // in LDS and are summed in split order, so the result does not depend on
-// timing.  S is derived on device from the actual tile count so that about
-// kDecodeWaves waves have work, and the grid is persistent: a fixed number of
-// blocks walks the item list, so nothing is launched for tiles that do not
-// exist (an all-remote batch costs one pass over counts).
+// timing.  S is derived on device from the actual tile count (decode_split),
+// and the grid is persistent: a fixed number of blocks walks the item list,
+// so nothing is launched for tiles that do not exist (an all-remote batch
+// costs one pass over counts).
 //
 // K is walked in 32-wide units; in unit u, lane group g = lane/16 holds
 // elements [32u + 8g, 32u + 8g + 8) of its A row and B row (the same K
@@ -448,7 +448,6 @@ hipError_t launch_control_k(const uint16_t* x, int K, int H, int F, int El, cons
 
 constexpr int kDecThreads = 1024;
 constexpr int kDecWaves = kDecThreads / 64;
-constexpr int kDecodeWaves = 4096;  // 16 waves on each of 256 compute units
 constexpr int kDecGrid = 256;
 // K units loaded before their MFMAs: 8 (512 bytes of each bf16 weight row);
 // 4 for MXFP4 GEMM1, whose widened operands would not fit in 128 VGPRs at 8
@@ -456,15 +455,37 @@ template <bool MX>
 constexpr int dec_unroll1() { return MX ? 4 : 8; }
 constexpr int kDecUnroll = 8;
 
-__device__ __forceinline__ int floor_pow2(int v) { return 1 << (31 - __clz(v)); }
+// K split S: a power of two <= 16 (the block's waves) with at least one K
+// unit per split, chosen by an estimate of the kernel's time.  An item (one
+// tile x 16/S column groups) keeps each wave busy for about
+// max(units/S, kSplitLatencyUnits) unit loads -- past a few units a wave's
+// time grows with the bytes it streams, below that the memory latency
+// dominates -- and `grid` persistent blocks take ceil(items / grid) rounds.
+// A split that leaves compute units idle (items just under a multiple of the
+// grid) loses to one that keeps them all streaming.  Ties go to the smaller
+// S (fewer partial sums to add).
+constexpr int kSplitLatencyUnits = 4;
 
-// K split: the largest power of two <= 16 that gives each split at least one
-// K unit and keeps the waves with work near kDecodeWaves.
-__device__ __forceinline__ int decode_split(int tiles, int col_groups, int units) {
-  const int64_t work = (int64_t)tiles * col_groups;  // waves with work when S = 1
-  int s = work >= kDecodeWaves ? 1 : floor_pow2((int)(kDecodeWaves / (work > 0 ? work : 1)));
-  s = min(s, kDecWaves);
-  return min(s, floor_pow2(units));
+__device__ __forceinline__ int decode_split(int tiles, int col_groups, int units, int grid) {
+  // The inputs are wave-uniform: make that visible so the search runs on the
+  // scalar unit with 32-bit divisions (a few hundred cycles at most).
+  tiles = __builtin_amdgcn_readfirstlane(tiles);
+  if (tiles <= 0 || (int64_t)tiles * col_groups >= ((int64_t)1 << 30)) return 1;  // nothing, or plenty, to spread
+  const unsigned g = (unsigned)grid;
+  int best = 1;
+  uint64_t best_cost = ~(uint64_t)0;
+  for (int s = 1; s <= kDecWaves && s <= units; s <<= 1) {
+    const unsigned cpb = (unsigned)(kDecWaves / s);
+    const unsigned items = (unsigned)tiles * (((unsigned)col_groups + cpb - 1) / cpb);
+    const unsigned rounds = (items + g - 1) / g;
+    const unsigned per = ((unsigned)units + s - 1) / (unsigned)s;
+    const uint64_t cost = (uint64_t)rounds * (per > kSplitLatencyUnits ? per : (unsigned)kSplitLatencyUnits);
+    if (cost < best_cost) {
+      best = s;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 __device__ __forceinline__ bf16x8 widen_mx8(uint32_t w, uint32_t e8) {
@@ -552,7 +573,7 @@ __global__ __launch_bounds__(kDecThreads) void ffn1_decode_kernel(
   }
   const int tiles = small ? tab.total : count_tiles(counts, El, 16);
   const int CG = F / 16, units = H / 32;
-  const int S = decode_split(tiles, CG, units);
+  const int S = decode_split(tiles, CG, units, gridDim.x);
   const int cpb = kDecWaves / S;         // column groups per item
   const int ipt = (CG + cpb - 1) / cpb;  // items per tile
   const int items = tiles * ipt;
@@ -645,7 +666,7 @@ __global__ __launch_bounds__(kDecThreads) void ffn2_decode_kernel(
   if (small) tab = load_tile_tab(counts, offsets, El, 16);
   const int tiles = small ? tab.total : count_tiles(counts, El, 16);
   const int CG = H / 16, units = F / 32;
-  const int S = decode_split(tiles, CG, units);
+  const int S = decode_split(tiles, CG, units, gridDim.x);
   const int cpb = kDecWaves / S;
   const int ipt = (CG + cpb - 1) / cpb;
   const int items = tiles * ipt;
@@ -730,6 +751,40 @@ hipError_t launch_decode(const uint16_t* x, int K, int H, int F, int El, const v
 // GEMM1 kernel (ffn1_decode_kernel<MX, true>) and the combine in the tail of
 // the GEMM2 kernel below, so the layer after the gate is two launches.
 
+// One tile's operands for a wave of the fused GEMM2: the n (<= kFusedUnits)
+// K units [u0, u0 + n) of its 16 weight rows and of the tile's act rows.
+constexpr int kFusedUnits = 4;
+
+template <bool MX>
+struct TileOperands {
+  WUnit<MX> b[kFusedUnits];
+  bf16x8 a[kFusedUnits];
+  int row0, nrows;
+
+  // Every slot is loaded (units past the wave's range re-read unit
+  // units - 1 and are not used), so no register keeps an older value.
+  __device__ __forceinline__ void load(const TileTab& tab, int tile, const uint16_t* __restrict__ act,
+                                       const void* __restrict__ w2, const uint8_t* __restrict__ w2s, int H, int F,
+                                       int cg, int u0, int units, int c, int g) {
+    int e = 0;
+    tab_find(tab, 16, tile, e, row0, nrows);
+    const uint16_t* ar = act + (int64_t)(row0 + (c < nrows ? c : 0)) * F;
+    const int64_t rw = (int64_t)e * H + cg * 16 + c;
+#pragma unroll
+    for (int j = 0; j < kFusedUnits; ++j) b[j].load(w2, w2s, rw, F, min(u0 + j, units - 1), g);
+#pragma unroll
+    for (int j = 0; j < kFusedUnits; ++j) a[j] = unit_bf16(ar, min(u0 + j, units - 1), g);
+  }
+
+  __device__ __forceinline__ f32x4 mma(int n) const {
+    f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < kFusedUnits; ++j)
+      if (j < n) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], b[j].get(), acc, 0, 0, 0);
+    return acc;
+  }
+};
+
 // GEMM2 with the combine in its tail.  Block b owns the 16 output columns
 // [16 cg, 16 cg + 16), cg = b, b + grid, ..., across every tile: the 16 waves
 // split the reduction 16 ways for one tile at a time, wave 0 adds the
@@ -737,7 +792,9 @@ hipError_t launch_decode(const uint16_t* x, int K, int H, int F, int El, const v
 // LDS.  When all tiles are done the block forms
 //   out[t, cols] = sum over k ascending, slot local, of w[t,k] * y[row, cols]
 // from LDS -- the combine kernel's arithmetic -- so y never goes to memory.
-template <bool MX, typename OT>
+// PIPE (at most kFusedUnits K units per wave, F <= 2048): the next tile's
+// loads are in flight while the current tile is reduced.
+template <bool MX, bool PIPE, typename OT>
 __global__ __launch_bounds__(kDecThreads) void ffn2_combine_kernel(
     const uint16_t* __restrict__ act, int H, int F, int El, const void* __restrict__ w2,
     const uint8_t* __restrict__ w2s, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
@@ -757,46 +814,66 @@ __global__ __launch_bounds__(kDecThreads) void ffn2_combine_kernel(
   const int CG = H / 16, units = F / 32;
   const int per = (units + kDecWaves - 1) / kDecWaves;
   const int u_begin = min(units, wave * per), u_end = min(units, u_begin + per);
+  const int n = u_end - u_begin;  // this wave's K units (wave-uniform)
   __syncthreads();  // srow, sw
 
+  // partial sums of one tile -> y values of its rows in ys
+  auto finish_tile = [&](f32x4 acc, int row0, int nrows) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][i][lane] = acc[i];
+    __syncthreads();
+    if (wave == 0) {
+      for (int sp = 1; sp < kDecWaves; ++sp) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += red[sp][i][lane];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = g * 4 + i;
+        if (m < nrows) ys[row0 + m][c] = bf16_bits_to_f32(f32_to_bf16_bits(acc[i]));
+      }
+    }
+    __syncthreads();  // red is rewritten by the next tile; ys complete
+  };
+
   for (int cg = blockIdx.x; cg < CG; cg += gridDim.x) {
-    for (int tile = 0; tile < tiles; ++tile) {
-      int e = 0, row0 = 0, nrows = 0;
-      tab_find(tab, 16, tile, e, row0, nrows);
-      f32x4 acc = {0, 0, 0, 0};
-      const uint16_t* ar = act + (int64_t)(row0 + (c < nrows ? c : 0)) * F;
-      const int64_t rw = (int64_t)e * H + cg * 16 + c;
-      int u = u_begin;
-      for (; u + kDecUnroll <= u_end; u += kDecUnroll) {
-        WUnit<MX> b[kDecUnroll];
-        bf16x8 a[kDecUnroll];
-#pragma unroll
-        for (int j = 0; j < kDecUnroll; ++j) b[j].load(w2, w2s, rw, F, u + j, g);
-#pragma unroll
-        for (int j = 0; j < kDecUnroll; ++j) a[j] = unit_bf16(ar, u + j, g);
-#pragma unroll
-        for (int j = 0; j < kDecUnroll; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], b[j].get(), acc, 0, 0, 0);
+    if constexpr (PIPE) {
+      // the operands of tile i + 1 are requested as soon as the MFMAs have
+      // consumed those of tile i, so they arrive during tile i's reduction
+      TileOperands<MX> op;
+      if (tiles > 0) op.load(tab, 0, act, w2, w2s, H, F, cg, u_begin, units, c, g);
+      for (int tile = 0; tile < tiles; ++tile) {
+        const f32x4 acc = op.mma(n);
+        const int row0 = op.row0, nrows = op.nrows;
+        if (tile + 1 < tiles) op.load(tab, tile + 1, act, w2, w2s, H, F, cg, u_begin, units, c, g);
+        finish_tile(acc, row0, nrows);
       }
-      for (; u < u_end; ++u) {
-        WUnit<MX> b;
-        b.load(w2, w2s, rw, F, u, g);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unit_bf16(ar, u, g), b.get(), acc, 0, 0, 0);
-      }
+    } else {
+      for (int tile = 0; tile < tiles; ++tile) {
+        int e = 0, row0 = 0, nrows = 0;
+        tab_find(tab, 16, tile, e, row0, nrows);
+        f32x4 acc = {0, 0, 0, 0};
+        const uint16_t* ar = act + (int64_t)(row0 + (c < nrows ? c : 0)) * F;
+        const int64_t rw = (int64_t)e * H + cg * 16 + c;
+        int u = u_begin;
+        for (; u + kDecUnroll <= u_end; u += kDecUnroll) {
+          WUnit<MX> b[kDecUnroll];
+          bf16x8 a[kDecUnroll];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[wave][i][lane] = acc[i];
-      __syncthreads();
-      if (wave == 0) {
-        for (int sp = 1; sp < kDecWaves; ++sp) {
+          for (int j = 0; j < kDecUnroll; ++j) b[j].load(w2, w2s, rw, F, u + j, g);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i] += red[sp][i][lane];
+          for (int j = 0; j < kDecUnroll; ++j) a[j] = unit_bf16(ar, u + j, g);
+#pragma unroll
+          for (int j = 0; j < kDecUnroll; ++j)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], b[j].get(), acc, 0, 0, 0);
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = g * 4 + i;
-          if (m < nrows) ys[row0 + m][c] = bf16_bits_to_f32(f32_to_bf16_bits(acc[i]));
+        for (; u < u_end; ++u) {
+          WUnit<MX> b;
+          b.load(w2, w2s, rw, F, u, g);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unit_bf16(ar, u, g), b.get(), acc, 0, 0, 0);
         }
+        finish_tile(acc, row0, nrows);
       }
-      __syncthreads();  // red is rewritten by the next tile; ys complete
     }
     for (int i = threadIdx.x; i < T * 16; i += kDecThreads) {
       const int t = i >> 4, col = i & 15;
@@ -825,12 +902,25 @@ hipError_t launch_fused_k(const uint16_t* x, int64_t T, int K, int H, int F, con
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || T == 0) return err;  // T == 0: counts and offsets (zeros) are written
   const unsigned grid = (unsigned)min(kDecGrid, H / 16);
-  if (out_dtype == MOE_BF16)
-    hipLaunchKernelGGL((ffn2_combine_kernel<MX, uint16_t>), dim3(grid), dim3(kDecThreads), 0, stream, act, H, F, El,
-                       w2, w2s, counts, offsets, s2r, tw, (int)T, K, static_cast<uint16_t*>(out));
-  else
-    hipLaunchKernelGGL((ffn2_combine_kernel<MX, float>), dim3(grid), dim3(kDecThreads), 0, stream, act, H, F, El,
-                       w2, w2s, counts, offsets, s2r, tw, (int)T, K, static_cast<float*>(out));
+  const bool pipe = (F / 32 + kDecWaves - 1) / kDecWaves <= kFusedUnits;
+  const dim3 g(grid), b(kDecThreads);
+  if (out_dtype == MOE_BF16) {
+    uint16_t* o = static_cast<uint16_t*>(out);
+    if (pipe)
+      hipLaunchKernelGGL((ffn2_combine_kernel<MX, true, uint16_t>), g, b, 0, stream, act, H, F, El, w2, w2s, counts,
+                         offsets, s2r, tw, (int)T, K, o);
+    else
+      hipLaunchKernelGGL((ffn2_combine_kernel<MX, false, uint16_t>), g, b, 0, stream, act, H, F, El, w2, w2s, counts,
+                         offsets, s2r, tw, (int)T, K, o);
+  } else {
+    float* o = static_cast<float*>(out);
+    if (pipe)
+      hipLaunchKernelGGL((ffn2_combine_kernel<MX, true, float>), g, b, 0, stream, act, H, F, El, w2, w2s, counts,
+                         offsets, s2r, tw, (int)T, K, o);
+    else
+      hipLaunchKernelGGL((ffn2_combine_kernel<MX, false, float>), g, b, 0, stream, act, H, F, El, w2, w2s, counts,
+                         offsets, s2r, tw, (int)T, K, o);
+  }
   return hipGetLastError();
 }
 
