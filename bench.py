@@ -3,8 +3,9 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
 
-A step is one pass of the whole path -- moe_topk_softmax -> moe_route_compact
--> moe_grouped_ffn -> moe_combine -- over one batch of the prefill layer
+A step is one pass of the whole path -- moe_topk_compact (the top-k softmax
+gate and the route compaction, the compaction's count pass inside the gate
+kernel) -> moe_grouped_ffn -> moe_combine -- over one batch of the prefill layer
 (T=4096 tokens, E=128 experts all local, top-8 renormalised, hidden 2048,
 expert FFN 768, bf16, seeded synthetic inputs already resident in HBM).
 `value` is tokens/s of that layer.  One JSON line goes to stdout; progress
@@ -191,20 +192,21 @@ def bench_prefill(args, dev):
     stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):
+        # gate + route compaction in one call (the compaction's count pass
+        # runs in the gate kernel), the grouped FFN, the combine
         if ev:
             ev[0].record(stream)
-        moe.moe_topk_softmax(logits, K, True, tw, tid, tei, stream=stream)
+        _, (counts, offsets, s2r, r2s) = moe.moe_topk_compact(logits, K, True, "softmax", None, E,
+                                                               gate_out=(tw, tid, tei), route_out=cmp_out,
+                                                               workspace=cws, stream=stream)
         if ev:
             ev[1].record(stream)
-        counts, offsets, s2r, r2s = moe.moe_route_compact(tid, None, E, out=cmp_out, workspace=cws, stream=stream)
-        if ev:
-            ev[2].record(stream)
         moe.moe_grouped_ffn(x, K, w1, w2, counts, offsets, r2s, y=y, workspace=fws, stream=stream, tiled=True)
         if ev:
-            ev[3].record(stream)
+            ev[2].record(stream)
         moe.moe_combine(y, tw, s2r, out=out, stream=stream)
         if ev:
-            ev[4].record(stream)
+            ev[3].record(stream)
 
     # The GPU raises its clocks only under sustained load (measured: the FFN
     # takes ~16% longer in the first ~0.2 s of back-to-back steps), so untimed
@@ -221,7 +223,7 @@ def bench_prefill(args, dev):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -229,7 +231,7 @@ def bench_prefill(args, dev):
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    names = ["gate", "compact", "grouped_ffn", "combine"]
+    names = ["gate_compact", "grouped_ffn", "combine"]
     per = {n: 0.0 for n in names}
     for ev in events:
         for j, n in enumerate(names):
@@ -255,7 +257,22 @@ def bench_prefill(args, dev):
     }
     log(f"[bench] prefill layer: {ms_per_step:.3f} ms/step, {T / (ms_per_step / 1e3):.0f} tokens/s; "
         + ", ".join(f"{n} {v:.3f} ms" for n, v in per.items()))
-    return c, ms_per_step, per, roofline, settle
+    # the remap boundary at prefill: gate then compaction as two calls vs the
+    # one call with the count pass fused into the gate (alternated replays)
+    # (no stream argument: the calls go to the current stream, which is the
+    # capture stream while a graph is recorded)
+    def separate():
+        moe.moe_topk_softmax(logits, K, True, tw, tid, tei)
+        moe.moe_route_compact(tid, None, E, out=cmp_out, workspace=cws)
+
+    def fused():
+        moe.moe_topk_compact(logits, K, True, "softmax", None, E, gate_out=(tw, tid, tei), route_out=cmp_out,
+                             workspace=cws)
+
+    t_sep, t_fus = ab_graph_ms(separate, fused, 400, dev)
+    gate_fusion = {"separate_ms": round(t_sep, 5), "fused_ms": round(t_fus, 5)}
+    log(f"[bench] prefill gate + compaction: separate {t_sep * 1e3:.1f} us, fused {t_fus * 1e3:.1f} us")
+    return c, ms_per_step, per, roofline, settle, gate_fusion
 
 
 def traffic_for(name):
@@ -502,8 +519,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
         return
-    c, ms, per, roofline, settle = bench_prefill(args, dev)
-    secondary = {}
+    c, ms, per, roofline, settle, gate_fusion = bench_prefill(args, dev)
+    secondary = {"prefill_gate_compaction": gate_fusion}
     if not args.no_secondary:
         reps = 50 if args.quick else 400
         secondary["gate"] = [bench_gate(dev, E, reps) for E in (128, 160)]

@@ -121,6 +121,34 @@ int moe_route_compact(const int32_t* topk_ids, int64_t T, int32_t K, const int32
 size_t moe_route_compact_workspace_bytes(int64_t T, int32_t K, int32_t E_local);
 
 /*
+ * moe_topk_compact -- the gate and the route compaction of one rank in one
+ * call, with the compaction's count pass inside the gate kernel.
+ * Sources: page "Upstream Reference: Deep-Spark xllm + vllm", section "Call
+ * Chain: MoE topk_softmax on BI-V100" (the gate); b70 lab note "MTP1 M2
+ * compact scheduler closure", design paragraph (counts and row prefix on
+ * device from topk_ids plus expert_map) and closing paragraph (remove the
+ * remap boundary).
+ *
+ * Computes exactly what moe_topk_softmax (scoring 0) or moe_topk_sigmoid
+ * (scoring 1) followed by moe_route_compact compute, bit for bit: the gate
+ * outputs, then counts / offsets / slot_to_row / row_to_slot of topk_ids
+ * under expert_map (E_global = E, the logits' expert count).  For bf16
+ * logits with E in {64, 96, 128, 160, 192}, K = 8 and T*K > 4096 the gate
+ * kernel also ranks each block's slots by local expert, so the separate
+ * count pass of the compaction disappears; other shapes run the two steps
+ * one after the other.
+ * Arguments: those of the two calls; workspace as for moe_route_compact
+ * (moe_route_compact_workspace_bytes(T, K, E_local)).  Limits and errors:
+ * the union of theirs; scoring other than 0 or 1 is MOE_ERR_UNSUPPORTED.
+ * T == 0 writes counts = 0 and offsets = 0 only.
+ */
+int moe_topk_compact(const void* logits, int logits_dtype, int64_t T, int32_t E, int32_t K, int32_t renormalize,
+                     int32_t scoring, float* topk_weights, int32_t* topk_ids, int32_t* token_expert_indices,
+                     const int32_t* expert_map, int32_t E_local, int32_t* counts, int32_t* offsets,
+                     int32_t* slot_to_row, int32_t* row_to_slot, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/*
  * moe_route_align -- block-aligned (padded) variant of the expert-grouped
  * layout, for grouped GEMMs that work on fixed-height row blocks.
  * Source: page "Upstream Reference: Deep-Spark xllm + vllm", section "File

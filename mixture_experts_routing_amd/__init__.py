@@ -19,7 +19,7 @@ _LIB = _lib.load()
 
 __all__ = [
     "moe_topk_softmax", "moe_topk_sigmoid", "moe_route_compact", "moe_route_align", "moe_grouped_ffn",
-    "moe_grouped_ffn_control", "moe_fused_experts", "moe_combine", "moe_pack_ffn_weights", "moe_layer",
+    "moe_grouped_ffn_control", "moe_fused_experts", "moe_topk_compact", "moe_combine", "moe_pack_ffn_weights", "moe_layer",
     "MOE_F32", "MOE_BF16", "MOE_MXFP4", "MOE_BF16_TILED", "MoeError", "library_path",
 ]
 
@@ -135,6 +135,42 @@ def moe_route_compact(topk_ids: torch.Tensor, expert_map: Optional[torch.Tensor]
                                   _ptr(offsets), _ptr(s2r), _ptr(r2s), _ptr(workspace), ws_bytes,
                                   _stream(stream, dev)), "moe_route_compact")
     return counts, offsets, s2r, r2s
+
+
+def moe_topk_compact(logits: torch.Tensor, K: int, renormalize: bool = False, scoring: str = "softmax",
+                     expert_map: Optional[torch.Tensor] = None, E_local: Optional[int] = None, gate_out=None,
+                     route_out=None, with_indices: bool = True, workspace: Optional[torch.Tensor] = None,
+                     stream=None):
+    """Gate and route compaction in one call (the compaction's count pass runs
+    inside the gate kernel where the shape allows).  logits [T, E]; scoring
+    "softmax" or "sigmoid".  Returns ((topk_weights, topk_ids,
+    token_expert_indices or None), (counts, offsets, slot_to_row, row_to_slot))."""
+    dev = _dev(logits, expert_map)
+    T, E = logits.shape
+    if E_local is None:
+        E_local = E
+    if scoring not in ("softmax", "sigmoid"):
+        raise MoeError(f"unknown scoring {scoring!r}")
+    if gate_out is None:
+        gate_out = (torch.empty((T, K), dtype=torch.float32, device=dev),
+                    torch.empty((T, K), dtype=torch.int32, device=dev),
+                    torch.empty((T, K), dtype=torch.int32, device=dev) if with_indices else None)
+    tw, tid, tei = gate_out
+    if route_out is None:
+        route_out = (torch.empty(E_local, dtype=torch.int32, device=dev),
+                     torch.empty(E_local + 1, dtype=torch.int32, device=dev),
+                     torch.empty(T * K, dtype=torch.int32, device=dev),
+                     torch.empty(T * K, dtype=torch.int32, device=dev))
+    counts, offsets, s2r, r2s = route_out
+    need = route_compact_workspace_bytes(T, K, E_local)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_LIB.moe_topk_compact(_ptr(logits), _dt(logits), T, E, K, int(renormalize),
+                                 0 if scoring == "softmax" else 1, _ptr(tw), _ptr(tid), _ptr(tei), _ptr(expert_map),
+                                 E_local, _ptr(counts), _ptr(offsets), _ptr(s2r), _ptr(r2s), _ptr(workspace),
+                                 ws_bytes, _stream(stream, dev)), "moe_topk_compact")
+    return gate_out, route_out
 
 
 def route_align_workspace_bytes(T: int, K: int, E_local: int) -> int:

@@ -24,6 +24,8 @@ SIGNATURES = {
     "moe_topk_sigmoid": (_int, [_p, _int, _i64, _i32, _i32, _i32, _p, _p, _p, _p]),
     "moe_route_compact": (_int, [_p, _i64, _i32, _p, _i32, _i32, _p, _p, _p, _p, _p, _sz, _p]),
     "moe_route_compact_workspace_bytes": (_sz, [_i64, _i32, _i32]),
+    "moe_topk_compact": (_int, [_p, _int, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _i32, _p, _p, _p, _p, _p,
+                                _sz, _p]),
     "moe_route_align": (_int, [_p, _i64, _i32, _p, _i32, _i32, _i32, _p, _p, _p, _p, _p, _sz, _p]),
     "moe_route_align_workspace_bytes": (_sz, [_i64, _i32, _i32]),
     "moe_grouped_ffn": (_int, [_p, _int, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _int, _p, _p, _p, _p, _int,

@@ -63,6 +63,27 @@ int moe_topk_sigmoid(const void* logits, int logits_dtype, int64_t T, int32_t E,
                                              token_expert_indices, static_cast<hipStream_t>(stream)));
 }
 
+int moe_topk_compact(const void* logits, int logits_dtype, int64_t T, int32_t E, int32_t K, int32_t renormalize,
+                     int32_t scoring, float* topk_weights, int32_t* topk_ids, int32_t* token_expert_indices,
+                     const int32_t* expert_map, int32_t E_local, int32_t* counts, int32_t* offsets,
+                     int32_t* slot_to_row, int32_t* row_to_slot, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  if (scoring != 0 && scoring != 1) return MOE_ERR_UNSUPPORTED;
+  const int st = check_gate(logits, logits_dtype, T, E, K, topk_weights, topk_ids);
+  if (st > 0) return st;  // st < 0: T == 0, the compaction still defines counts and offsets
+  if (E_local < 1 || E_local > E) return MOE_ERR_INVALID_ARG;
+  if (!expert_map && E_local != E) return MOE_ERR_INVALID_ARG;
+  if (E_local > 768) return MOE_ERR_UNSUPPORTED;
+  if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
+  const int64_t N = T * K;
+  if (N > 0 && (!slot_to_row || !row_to_slot)) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe::route_compact_workspace_bytes(N, E_local);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_topk_compact(logits, logits_dtype, T, E, K, renormalize != 0, scoring, topk_weights,
+                                             topk_ids, token_expert_indices, expert_map, E_local, counts, offsets,
+                                             slot_to_row, row_to_slot, workspace, static_cast<hipStream_t>(stream)));
+}
+
 size_t moe_route_compact_workspace_bytes(int64_t T, int32_t K, int32_t E_local) {
   if (T <= 0 || K <= 0 || E_local <= 0) return 0;
   return moe::route_compact_workspace_bytes(T * K, E_local);

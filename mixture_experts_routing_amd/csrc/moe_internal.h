@@ -121,6 +121,46 @@ __device__ __forceinline__ int local_expert(int id, const int32_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
+// stable counting sort of slots by local expert (route compaction), pieces
+// shared by the compaction kernels and the gate kernel that fuses the count
+// pass: the multi-block compaction cuts the slots into blocks of
+// kCompactBlockSlots (thread i of block b holds slot b * kCompactBlockSlots + i)
+
+constexpr int kCompactWaves = 16;
+constexpr int kCompactBlockSlots = kCompactWaves * 64;  // 1024
+constexpr int kCompactSingleMax = 4096;                 // one block handles up to this many slots
+
+// For the 64 lanes of a wave holding local ids l (-1 = remote/absent): the
+// number of lower lanes with the same id, and the number with that id.
+__device__ __forceinline__ void wave_group_rank(int l, int lane, int& below, int& total) {
+  below = 0;
+  total = 0;
+#pragma unroll 16
+  for (int j = 0; j < 64; ++j) {
+    const int lj = __builtin_amdgcn_readlane(l, j);
+    const int eq = (lj == l) ? 1 : 0;
+    total += eq;
+    below += (j < lane) ? eq : 0;
+  }
+}
+
+// Per-expert exclusive prefix over the kCompactWaves rows of run[w*El + e]
+// (every thread of the block takes experts e = tid, tid + blockDim.x, ...);
+// each expert's total goes to cnt[e].
+__device__ __forceinline__ void prefix_over_compact_waves(int* __restrict__ run, int El, int* __restrict__ cnt) {
+  for (int e = threadIdx.x; e < El; e += blockDim.x) {
+    int acc = 0;
+#pragma unroll
+    for (int w = 0; w < kCompactWaves; ++w) {
+      const int c = run[w * El + e];
+      run[w * El + e] = acc;
+      acc += c;
+    }
+    cnt[e] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host-side launchers (one per kernel family), called after validation
 
 hipError_t launch_topk_softmax(const void* logits, int logits_dtype, int64_t T, int E, int K,
@@ -135,6 +175,21 @@ hipError_t launch_route_compact(const int32_t* topk_ids, int64_t N, const int32_
                                 int E_global, int E_local, int32_t* counts, int32_t* offsets,
                                 int32_t* slot_to_row, int32_t* row_to_slot, void* workspace,
                                 hipStream_t stream);
+
+// second phase of the multi-block compaction: from the per-block counts
+// block_counts [B][El] and the in-block ranks parked in s2r, the expert
+// counts and offsets and both permutations (N > kCompactSingleMax)
+hipError_t launch_compact_scatter_phase(const int32_t* topk_ids, int64_t N, const int32_t* expert_map, int E_global,
+                                        int E_local, int32_t* block_counts, int32_t* counts, int32_t* offsets,
+                                        int32_t* slot_to_row, int32_t* row_to_slot, hipStream_t stream);
+
+// gate and route compaction in one call; the count pass of the compaction
+// runs inside the gate kernel where the shape allows (scoring 0 softmax, 1
+// sigmoid)
+hipError_t launch_topk_compact(const void* logits, int logits_dtype, int64_t T, int E, int K, int renormalize,
+                               int scoring, float* w, int32_t* ids, int32_t* tei, const int32_t* expert_map,
+                               int E_local, int32_t* counts, int32_t* offsets, int32_t* slot_to_row,
+                               int32_t* row_to_slot, void* workspace, hipStream_t stream);
 
 size_t route_align_workspace_bytes(int64_t N, int E_local);
 hipError_t launch_route_align(const int32_t* topk_ids, int64_t N, const int32_t* expert_map, int E_global,

@@ -28,28 +28,19 @@
 namespace moe {
 namespace {
 
-constexpr int kWaves = 16;
+constexpr int kWaves = kCompactWaves;
 constexpr int kThreads = kWaves * 64;
 constexpr int kGroupsSingle = 4;                       // 64-slot groups per wave, single-block path
-constexpr int kSingleMax = kWaves * kGroupsSingle * 64;  // 4096 slots
-constexpr int kBlockSlots = kWaves * 64;               // slots per block, multi-block path
+constexpr int kSingleMax = kCompactSingleMax;          // 4096 slots
+constexpr int kBlockSlots = kCompactBlockSlots;        // slots per block, multi-block path
+static_assert(kSingleMax == kWaves * kGroupsSingle * 64, "single-block capacity");
 
 __device__ __forceinline__ int local_of(int id, const int32_t* __restrict__ emap, int Eg, int El) {
   return local_expert(id, emap, Eg, El);
 }
 
-// For a group of 64 lanes holding local ids l (-1 = remote/absent): the
-// number of lower lanes with the same id, and the total with that id.
 __device__ __forceinline__ void group_rank(int l, int lane, int& below, int& total) {
-  below = 0;
-  total = 0;
-#pragma unroll 16
-  for (int j = 0; j < 64; ++j) {
-    const int lj = __builtin_amdgcn_readlane(l, j);
-    const int eq = (lj == l) ? 1 : 0;
-    total += eq;
-    below += (j < lane) ? eq : 0;
-  }
+  wave_group_rank(l, lane, below, total);
 }
 
 // Ranks the 64-slot groups [first_slot + 64*g, ...) of one wave; returns the
@@ -106,19 +97,8 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total)
   return r;
 }
 
-// Per-expert exclusive prefix over the kWaves rows of run[w*El + e]; each
-// expert's total goes to cnt[e].
 __device__ __forceinline__ void prefix_over_waves(int* __restrict__ run, int El, int* __restrict__ cnt) {
-  for (int e = threadIdx.x; e < El; e += kThreads) {
-    int acc = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const int c = run[w * El + e];
-      run[w * El + e] = acc;
-      acc += c;
-    }
-    cnt[e] = acc;
-  }
+  prefix_over_compact_waves(run, El, cnt);
 }
 
 // Exclusive scan of cnt[0..El) into offs[0..El]; El <= kThreads.
@@ -303,7 +283,19 @@ __global__ __launch_bounds__(kThreads) void compact_scan_scatter_kernel(
   const int e = threadIdx.x;  // El <= kThreads: one expert per thread
   int tot = 0, pre = 0;
   if (e < El) {
-    for (int bb = 0; bb < B; ++bb) {
+    // 8 count loads in flight at a time (independent, L2-resident)
+    int bb = 0;
+    for (; bb + 8 <= B; bb += 8) {
+      int c[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c[j] = block_counts[(int64_t)(bb + j) * El + e];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        tot += c[j];
+        pre += bb + j < b ? c[j] : 0;
+      }
+    }
+    for (; bb < B; ++bb) {
       const int c = block_counts[(int64_t)bb * El + e];
       tot += c;
       pre += bb < b ? c : 0;
@@ -459,6 +451,14 @@ hipError_t launch_route_compact(const int32_t* ids, int64_t N, const int32_t* em
                      sizeof(int) * (size_t)kWaves * El, stream, ids, N, emap, Eg, El, bc, s2r);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  return launch_compact_scatter_phase(ids, N, emap, Eg, El, bc, counts, offsets, s2r, r2s, stream);
+}
+
+hipError_t launch_compact_scatter_phase(const int32_t* ids, int64_t N, const int32_t* emap, int Eg, int El,
+                                        int32_t* bc, int32_t* counts, int32_t* offsets, int32_t* s2r, int32_t* r2s,
+                                        hipStream_t stream) {
+  const int64_t B = (N + kBlockSlots - 1) / kBlockSlots;
+  hipError_t err;
   if (B <= kFusedMaxBlocks) {
     hipLaunchKernelGGL(compact_scan_scatter_kernel, dim3((unsigned)B), dim3(kThreads),
                        sizeof(int) * ((size_t)El + kWaves + 1), stream, ids, N, emap, Eg, El, bc, (int)B, counts,

@@ -337,14 +337,16 @@ __device__ __forceinline__ void merge_top8(int32_t* a, const int32_t* b, int nb)
   cx(a[0], a[1]); cx(a[2], a[3]); cx(a[4], a[5]); cx(a[6], a[7]);
 }
 
+// Row t of the bf16 fast gate on the 8-lane group of this thread (lane q =
+// threadIdx.x % 8 holds experts [qV, qV+V) and finishes rank q).  Stores the
+// row's outputs and returns this lane's chosen expert id, or -1 (q >= K or
+// t >= T).
 template <int V, bool SIG>
-__global__ __launch_bounds__(kBlock) void topk8_bf16_kernel(const uint16_t* __restrict__ logits, int64_t T, int K,
-                                                            int renorm, float* __restrict__ w_out,
-                                                            int32_t* __restrict__ id_out,
-                                                            int32_t* __restrict__ tei_out) {
+__device__ __forceinline__ int gate8_group(const uint16_t* __restrict__ logits, int64_t T, int K, int renorm,
+                                           int64_t t, float* __restrict__ w_out, int32_t* __restrict__ id_out,
+                                           int32_t* __restrict__ tei_out) {
   constexpr int G = 8, E = G * V, W = V / 2;  // W: 32-bit words per lane
   const int q = threadIdx.x & 7;
-  const int64_t t = (int64_t)blockIdx.x * (kBlock / G) + (threadIdx.x >> 3);
   const bool row_ok = t < T;
   const int64_t tc = row_ok ? t : 0;  // out-of-range rows read row 0, store nothing
 
@@ -449,10 +451,51 @@ __global__ __launch_bounds__(kBlock) void topk8_bf16_kernel(const uint16_t* __re
   const float norm = renorm ? group_sum_f32<G>(e) : denom;
   if (row_ok && q < K) {
     const int64_t o = t * K + q;
+    const int id = Keys<uint16_t>::index(mine);
     w_out[o] = (SIG && !renorm) ? e : e / norm;
-    id_out[o] = Keys<uint16_t>::index(mine);
+    id_out[o] = id;
     if (tei_out) tei_out[o] = (int32_t)((int64_t)q * T + t);
+    return id;
   }
+  return -1;
+}
+
+template <int V, bool SIG>
+__global__ __launch_bounds__(kBlock) void topk8_bf16_kernel(const uint16_t* __restrict__ logits, int64_t T, int K,
+                                                            int renorm, float* __restrict__ w_out,
+                                                            int32_t* __restrict__ id_out,
+                                                            int32_t* __restrict__ tei_out) {
+  const int64_t t = (int64_t)blockIdx.x * (kBlock / 8) + (threadIdx.x >> 3);
+  gate8_group<V, SIG>(logits, T, K, renorm, t, w_out, id_out, tei_out);
+}
+
+// The gate with the count pass of the route compaction fused in (K = 8): a
+// block of kCompactBlockSlots threads takes 128 rows, so thread i ends up
+// holding slot b * kCompactBlockSlots + i -- the slot the compaction's count
+// kernel gives that thread -- and does that kernel's work on it: the slot's
+// rank among equal local ids of its block (in slot order) parked in s2r, and
+// the block's per-expert counts in block_counts[b][El].  The compaction's
+// scan/scatter phase follows as a separate launch.
+template <int V, bool SIG>
+__global__ __launch_bounds__(kCompactBlockSlots) void topk8_count_kernel(
+    const uint16_t* __restrict__ logits, int64_t T, int renorm, float* __restrict__ w_out,
+    int32_t* __restrict__ id_out, int32_t* __restrict__ tei_out, const int32_t* __restrict__ emap, int Eg, int El,
+    int32_t* __restrict__ block_counts, int32_t* __restrict__ s2r) {
+  extern __shared__ int run[];  // [kCompactWaves][El]: per-wave counts, then their prefix
+  for (int i = threadIdx.x; i < kCompactWaves * El; i += kCompactBlockSlots) run[i] = 0;
+  const int64_t t = (int64_t)blockIdx.x * (kCompactBlockSlots / 8) + (threadIdx.x >> 3);
+  const int id = gate8_group<V, SIG>(logits, T, 8, renorm, t, w_out, id_out, tei_out);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l = id >= 0 ? local_expert(id, emap, Eg, El) : -1;
+  int below, total;
+  wave_group_rank(l, lane, below, total);
+  __syncthreads();  // run is zero
+  int* runw = run + wave * El;
+  if (l >= 0 && below == total - 1) runw[l] = total;  // one writer per distinct id of the wave
+  __syncthreads();
+  prefix_over_compact_waves(run, El, block_counts + (int64_t)blockIdx.x * El);
+  __syncthreads();
+  if (l >= 0) s2r[(int64_t)blockIdx.x * kCompactBlockSlots + threadIdx.x] = runw[l] + below;
 }
 
 template <int V, bool SIG>
@@ -508,6 +551,59 @@ hipError_t launch_topk_softmax(const void* logits, int logits_dtype, int64_t T, 
 hipError_t launch_topk_sigmoid(const void* logits, int logits_dtype, int64_t T, int E, int K, int renormalize,
                                float* w, int32_t* ids, int32_t* tei, hipStream_t stream) {
   return launch_gate<true>(logits, logits_dtype, T, E, K, renormalize, w, ids, tei, stream);
+}
+
+namespace {
+template <int V, bool SIG>
+hipError_t launch_count_fused(const uint16_t* logits, int64_t T, int renorm, float* w, int32_t* ids, int32_t* tei,
+                              const int32_t* emap, int Eg, int El, int32_t* bc, int32_t* s2r, hipStream_t stream) {
+  const int64_t blocks = (T + kCompactBlockSlots / 8 - 1) / (kCompactBlockSlots / 8);
+  hipLaunchKernelGGL((topk8_count_kernel<V, SIG>), dim3((unsigned)blocks), dim3(kCompactBlockSlots),
+                     sizeof(int) * (size_t)kCompactWaves * El, stream, logits, T, renorm, w, ids, tei, emap, Eg, El,
+                     bc, s2r);
+  return hipGetLastError();
+}
+
+template <bool SIG>
+hipError_t dispatch_count_fused(int V, const uint16_t* logits, int64_t T, int renorm, float* w, int32_t* ids,
+                                int32_t* tei, const int32_t* emap, int Eg, int El, int32_t* bc, int32_t* s2r,
+                                hipStream_t stream) {
+  switch (V) {
+    case 8: return launch_count_fused<8, SIG>(logits, T, renorm, w, ids, tei, emap, Eg, El, bc, s2r, stream);
+    case 12: return launch_count_fused<12, SIG>(logits, T, renorm, w, ids, tei, emap, Eg, El, bc, s2r, stream);
+    case 16: return launch_count_fused<16, SIG>(logits, T, renorm, w, ids, tei, emap, Eg, El, bc, s2r, stream);
+    case 20: return launch_count_fused<20, SIG>(logits, T, renorm, w, ids, tei, emap, Eg, El, bc, s2r, stream);
+    default: return launch_count_fused<24, SIG>(logits, T, renorm, w, ids, tei, emap, Eg, El, bc, s2r, stream);
+  }
+}
+}  // namespace
+
+hipError_t launch_topk_compact(const void* logits, int logits_dtype, int64_t T, int E, int K, int renormalize,
+                               int scoring, float* w, int32_t* ids, int32_t* tei, const int32_t* emap, int El,
+                               int32_t* counts, int32_t* offsets, int32_t* s2r, int32_t* r2s, void* workspace,
+                               hipStream_t stream) {
+  const int64_t N = T * K;
+  const int V = E / 8;
+  const int align = (V % 8 == 0) ? 16 : 8;
+  const bool fused = logits_dtype == MOE_BF16 && K == 8 && N > kCompactSingleMax && E % 8 == 0 &&
+                     (V == 8 || V == 12 || V == 16 || V == 20 || V == 24) && (uintptr_t)logits % align == 0 &&
+                     (E * 2) % align == 0;
+  if (fused) {
+    const uint16_t* p = static_cast<const uint16_t*>(logits);
+    int32_t* bc = static_cast<int32_t*>(workspace);  // [B][El], as the compaction's count kernel uses it
+    hipError_t err = scoring ? dispatch_count_fused<true>(V, p, T, renormalize, w, ids, tei, emap, E, El, bc, s2r,
+                                                          stream)
+                             : dispatch_count_fused<false>(V, p, T, renormalize, w, ids, tei, emap, E, El, bc, s2r,
+                                                           stream);
+    if (err != hipSuccess) return err;
+    return launch_compact_scatter_phase(ids, N, emap, E, El, bc, counts, offsets, s2r, r2s, stream);
+  }
+  if (T > 0) {
+    const hipError_t err = scoring ? launch_gate<true>(logits, logits_dtype, T, E, K, renormalize, w, ids, tei, stream)
+                                   : launch_gate<false>(logits, logits_dtype, T, E, K, renormalize, w, ids, tei, stream);
+    if (err != hipSuccess) return err;
+  }
+  return launch_route_compact(ids, N, emap, E, El, counts, offsets, s2r, r2s, workspace, stream);
 }
 
 }  // namespace moe

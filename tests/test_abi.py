@@ -119,3 +119,21 @@ def test_fused_experts_validation(lib):
     assert need == 2 * 6 * 2048 * 2             # the bf16 act rows
     assert f(*args(wsb=need - 1)) == 4
     assert f(*args(x=ctypes.c_void_p(0x1002))) == 1  # x must be 16-byte aligned
+
+
+@_no_gpu
+def test_topk_compact_validation(lib):
+    f = lib.moe_topk_compact
+    def args(T=4096, E=128, K=8, scoring=0, emap=NULL, El=128, ws=FAKE, wsb=1 << 40, counts=FAKE, s2r=FAKE):
+        return (FAKE, 1, T, E, K, 1, scoring, FAKE, FAKE, NULL, emap, El, counts, FAKE, s2r, FAKE, ws, wsb, NULL)
+
+    assert f(*args(scoring=2)) == 2             # unknown scoring
+    assert f(*args(K=9, E=8)) == 1              # K > E
+    assert f(*args(El=40)) == 1                 # no map while E_local != E
+    assert f(*args(El=200, emap=FAKE)) == 1     # E_local > E
+    assert f(*args(E=1000, El=800, emap=FAKE)) == 2  # E_local > 768
+    assert f(*args(counts=NULL)) == 1
+    assert f(*args(s2r=NULL)) == 1
+    assert f(*args(ws=NULL)) == 4               # 32768 slots need the count table
+    need = lib.moe_route_compact_workspace_bytes(4096, 8, 128)
+    assert f(*args(wsb=need - 1)) == 4
