@@ -214,28 +214,39 @@ __device__ __forceinline__ void tile_kloop(const Tile& cur, const Tile& nxt, __a
     for (int nb = 0; nb < 2; ++nb)
       b_addr[nb][ks] = (BM + wn * 64 + nb * 32 + r32) * kRowBytes + (((2 * ks + hi) ^ sw) * 16);
   }
-  // All fragments of the step are requested before the first MFMA (the
-  // sched_barrier keeps the compiler from sinking the reads next to their
-  // uses), so the reads of the second K half arrive while the first half runs
-  // on the matrix core.
+  // The fragments of the step's first K half are requested first; its MFMAs
+  // then alternate with the reads of the second half (one read after each
+  // MFMA), so the first MFMAs do not queue behind the whole step's LDS reads.
   auto compute = [&](int slot) {
     const uint8_t* base = lds + slot * STAGE;
     bf16x8 a[2][LIVE > 0 ? LIVE : 1], b[2][2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int nb = 0; nb < 2; ++nb) b[0][nb] = *reinterpret_cast<const bf16x8*>(base + b_addr[nb][0]);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) b[ks][nb] = *reinterpret_cast<const bf16x8*>(base + b_addr[nb][ks]);
-#pragma unroll
-      for (int mb = 0; mb < LIVE; ++mb) a[ks][mb] = *reinterpret_cast<const bf16x8*>(base + a_addr[mb][ks]);
-    }
+    for (int mb = 0; mb < LIVE; ++mb) a[0][mb] = *reinterpret_cast<const bf16x8*>(base + a_addr[mb][0]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int nb = 0; nb < 2; ++nb) b[1][nb] = *reinterpret_cast<const bf16x8*>(base + b_addr[nb][1]);
 #pragma unroll
-      for (int mb = 0; mb < LIVE; ++mb) {
-        acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][mb], b[ks][0], acc[mb][0], 0, 0, 0);
-        acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][mb], b[ks][1], acc[mb][1], 0, 0, 0);
-      }
+    for (int mb = 0; mb < LIVE; ++mb) a[1][mb] = *reinterpret_cast<const bf16x8*>(base + a_addr[mb][1]);
+#pragma unroll
+    for (int mb = 0; mb < LIVE; ++mb) {
+      acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][mb], b[0][0], acc[mb][0], 0, 0, 0);
+      acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][mb], b[0][1], acc[mb][1], 0, 0, 0);
+    }
+    // scheduling groups (mask 0x008: MFMA, 0x100: LDS read)
+#pragma unroll
+    for (int i = 0; i < LIVE + 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if constexpr (LIVE > 2) __builtin_amdgcn_sched_group_barrier(0x008, LIVE - 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mb = 0; mb < LIVE; ++mb) {
+      acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][mb], b[1][0], acc[mb][0], 0, 0, 0);
+      acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][mb], b[1][1], acc[mb][1], 0, 0, 0);
+    }
   };
   for (int kt = 0; kt < KT; ++kt, ++g) {
     // own loads of step g have landed once only the kStages-2 newer steps remain
