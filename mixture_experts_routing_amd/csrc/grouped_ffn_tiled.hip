@@ -45,6 +45,10 @@ constexpr int kBN = kPanelRows; // weight rows per block
 constexpr int kStages = 4;      // LDS ring: steps k+1, k+2 in flight while step k computes
 constexpr int kRowBytes = kBK * 2;
 constexpr int kGrid = 256;       // persistent blocks: one per compute unit
+// cache policy of the weight loads: non-temporal (each weight panel is read
+// by one block, once), so the streamed weights do not push the re-read A
+// rows out of the caches
+constexpr int kWeightCachePolicy = 2;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -199,7 +203,7 @@ __device__ __forceinline__ void tile_kloop(const Tile& cur, const Tile& nxt, __a
 #pragma unroll
       for (int i = 0; i < U::B; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(base + BM * kRowBytes + (wave - 4 + 4 * i) * 1024),
-                                                 16, t.src[i], skb, 0, 0);
+                                                 16, t.src[i], skb, 0, kWeightCachePolicy);
     }
   };
   // fragment addresses (bytes within a stage): lane l reads row R, logical
@@ -312,7 +316,8 @@ __global__ __launch_bounds__(kTThreads) void ffn_tiled_kernel(
 #pragma unroll
         for (int i = 0; i < U::B; ++i)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(cur.rb, (lds_ptr_t)(base + BM * kRowBytes + (wave - 4 + 4 * i) * 1024),
-                                                   16, cur.src[i], s * (PACKED ? kBN * kRowBytes : kRowBytes), 0, 0);
+                                                   16, cur.src[i], s * (PACKED ? kBN * kRowBytes : kRowBytes), 0,
+                                                   kWeightCachePolicy);
       }
     }
   }
