@@ -541,14 +541,19 @@ struct FusedRoutes {
 
 // GEMM1 + silu_and_mul for the decode regime.  Same operands as
 // ffn1_stream_kernel; with ROUTES, counts/offsets/r2s are unused and the
-// route table comes from `fr` (El <= 64, N <= 64).
+// route table comes from `fr` (El <= 64, N <= 64).  A column group is 8 act
+// columns: the 16 columns of one MFMA tile are their 8 gate rows of W1
+// (lanes c < 8) and the matching 8 up rows (lanes c >= 8), so one MFMA
+// yields both halves and a lane exchange (c <-> c + 8) pairs them for
+// silu(gate) * up -- twice as many items as 16 gate + 16 up columns would
+// give, which keeps every compute unit streaming when few tiles exist.
 template <bool MX, bool ROUTES>
 __global__ __launch_bounds__(kDecThreads) void ffn1_decode_kernel(
     const uint16_t* __restrict__ x, int K, int H, int F, int El, const void* __restrict__ w1,
     const uint8_t* __restrict__ w1s, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ r2s, uint16_t* __restrict__ act, FusedRoutes fr) {
   constexpr int U = dec_unroll1<MX>();
-  __shared__ float red[kDecWaves][8][64];
+  __shared__ float red[kDecWaves][4][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
   const bool small = ROUTES || El <= 64;  // uniform
   TileTab tab{};
@@ -572,7 +577,7 @@ __global__ __launch_bounds__(kDecThreads) void ffn1_decode_kernel(
     tab = load_tile_tab(counts, offsets, El, 16);
   }
   const int tiles = small ? tab.total : count_tiles(counts, El, 16);
-  const int CG = F / 16, units = H / 32;
+  const int CG = F / 8, units = H / 32;  // column groups of 8 act columns
   const int S = decode_split(tiles, CG, units, gridDim.x);
   const int cpb = kDecWaves / S;         // column groups per item
   const int ipt = (CG + cpb - 1) / cpb;  // items per tile
@@ -588,7 +593,7 @@ __global__ __launch_bounds__(kDecThreads) void ffn1_decode_kernel(
     else find_tile(counts, offsets, El, 16, tile, e, row0, nrows);
     const int cg = cb * cpb + cgl;
     const bool active = cg < CG;
-    f32x4 ag = {0, 0, 0, 0}, au = {0, 0, 0, 0};
+    f32x4 acc = {0, 0, 0, 0};
     if (active) {
       // rows past the tile's end reuse the first row; their results are dropped
       const int r = row0 + (c < nrows ? c : 0);
@@ -597,57 +602,44 @@ __global__ __launch_bounds__(kDecThreads) void ffn1_decode_kernel(
       else slot = r2s[r];
       const int tok = slot / K;
       const uint16_t* xr = x + (int64_t)tok * H;
-      const int64_t rg = (int64_t)e * 2 * F + cg * 16 + c, ru = rg + F;
+      // W1 row of this lane's MFMA column: gate row (c < 8) or up row
+      const int64_t rw = (int64_t)e * 2 * F + (c >> 3) * F + cg * 8 + (c & 7);
       int u = u_begin;
       for (; u + U <= u_end; u += U) {
-        WUnit<MX> bg[U], bu[U];
+        WUnit<MX> b[U];
         bf16x8 a[U];
 #pragma unroll
-        for (int j = 0; j < U; ++j) {
-          bg[j].load(w1, w1s, rg, H, u + j, g);
-          bu[j].load(w1, w1s, ru, H, u + j, g);
-        }
+        for (int j = 0; j < U; ++j) b[j].load(w1, w1s, rw, H, u + j, g);
 #pragma unroll
         for (int j = 0; j < U; ++j) a[j] = unit_bf16(xr, u + j, g);
 #pragma unroll
-        for (int j = 0; j < U; ++j) {
-          ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], bg[j].get(), ag, 0, 0, 0);
-          au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], bu[j].get(), au, 0, 0, 0);
-        }
+        for (int j = 0; j < U; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], b[j].get(), acc, 0, 0, 0);
       }
       for (; u < u_end; ++u) {
-        WUnit<MX> bg, bu;
-        bg.load(w1, w1s, rg, H, u, g);
-        bu.load(w1, w1s, ru, H, u, g);
-        const bf16x8 a = unit_bf16(xr, u, g);
-        ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bg.get(), ag, 0, 0, 0);
-        au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bu.get(), au, 0, 0, 0);
+        WUnit<MX> b;
+        b.load(w1, w1s, rw, H, u, g);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unit_bf16(xr, u, g), b.get(), acc, 0, 0, 0);
       }
     }
     if (S > 1) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        red[wave][i][lane] = ag[i];
-        red[wave][4 + i][lane] = au[i];
-      }
+      for (int i = 0; i < 4; ++i) red[wave][i][lane] = acc[i];
       __syncthreads();
       if (ks == 0) {
         for (int sp = 1; sp < S; ++sp) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            ag[i] += red[wave + sp][i][lane];
-            au[i] += red[wave + sp][4 + i][lane];
-          }
+          for (int i = 0; i < 4; ++i) acc[i] += red[wave + sp][i][lane];
         }
       }
       __syncthreads();  // red is rewritten by the next item
     }
     if (ks == 0 && active) {
-      const int n = cg * 16 + c;
+      const int n = cg * 8 + (c & 7);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = g * 4 + i;
-        if (m < nrows) act[(int64_t)(row0 + m) * F + n] = f32_to_bf16_bits(silu_f32(ag[i]) * au[i]);
+        const float up = __shfl_xor(acc[i], 8, 64);  // lane c ^ 8: the up value of the same column
+        if (c < 8 && m < nrows) act[(int64_t)(row0 + m) * F + n] = f32_to_bf16_bits(silu_f32(acc[i]) * up);
       }
     }
   }
