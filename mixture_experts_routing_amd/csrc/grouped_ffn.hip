@@ -433,8 +433,9 @@ hipError_t launch_control_k(const uint16_t* x, int K, int H, int F, int El, cons
 // With a handful of rows per expert the FFN is a weight stream.  One wave per
 // 16 output columns of a 16-row M-tile leaves too few waves in flight to keep
 // HBM busy when only one or two experts are hit, so each 1024-thread block
-// takes an item -- one M-tile and 16/S groups of 16 columns -- and its 16
-// waves split the reduction dimension S ways.  The partial accumulators meet
+// takes an item -- one M-tile and 16/S column groups (16 output columns of
+// GEMM2; 8 act columns, i.e. 8 gate and 8 up weight rows, of GEMM1) -- and
+// its 16 waves split the reduction dimension S ways.  The partial accumulators meet
 // in LDS and are summed in split order, so the result does not depend on
 // timing.  S is derived on device from the actual tile count (decode_split),
 // and the grid is persistent: a fixed number of blocks walks the item list,
