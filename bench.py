@@ -503,8 +503,8 @@ def cpu_baseline(c, n_tokens, min_seconds=10.0, max_reps=20):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 (the path would shard by "
-                                   "experts across GPUs, which is not built)"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1 (the path would shard "
+                                   "by experts across GPUs; that is not implemented)"}))
         sys.exit(2)
     import torch
 
