@@ -63,6 +63,9 @@ def parse():
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB five times (the reference kernel "
                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exit")
+    p.add_argument("--profile", default="", metavar="WHAT",
+                   help="only run one secondary for a kernel trace and exit: 'gate' (the five gate "
+                        "configurations) or 'decode:PATTERN' (one decode route pattern, every path)")
     return p.parse_args()
 
 
@@ -330,7 +333,7 @@ def bench_gate(dev, E, reps, scoring="softmax"):
 # secondary: decode layer per route pattern
 
 
-def bench_decode(dev, reps):
+def bench_decode(dev, reps, only=None):
     import numpy as np
     import torch
 
@@ -348,6 +351,8 @@ def bench_decode(dev, reps):
     res = {}
     nvar = 8  # rotated copies of each pattern: consecutive calls touch different experts
     for pat in synth.decode_patterns():
+        if only is not None and pat != only:
+            continue
         base = synth.decode_case(pat, "contiguous", seed=0, with_weights=False)
         x = bf16_dev(base.x, dev)
         tw = f32_dev(base.topk_weights, dev)
@@ -424,6 +429,8 @@ def bench_decode(dev, reps):
             d.update({"ffn_weight_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
         res[pat] = d
         log(f"[bench] decode {pat}: " + json.dumps(d))
+    if only is not None:
+        return {"patterns": res}
     nonempty = [p for p in res if res[p]["local_experts"] > 0]
     worst = min(nonempty, key=lambda p: res[p]["hbm_frac"])
     saved = {p: res[p]["projected_saved_ms_43_layers"] for p in res}
@@ -518,6 +525,16 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+        return
+    if args.profile:
+        if args.profile == "gate":
+            res = [bench_gate(dev, E, 64) for E in (128, 160)]
+            res += [bench_gate(dev, E, 64, "sigmoid") for E in (128, 160, 256)]
+        elif args.profile.startswith("decode:"):
+            res = bench_decode(dev, 5, only=args.profile.split(":", 1)[1])
+        else:
+            raise SystemExit(f"unknown --profile {args.profile!r}")
+        print(json.dumps({"profile": args.profile, "result": res}), flush=True)
         return
     c, ms, per, roofline, settle, gate_fusion = bench_prefill(args, dev)
     secondary = {"prefill_gate_compaction": gate_fusion}
