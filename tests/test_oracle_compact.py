@@ -214,3 +214,17 @@ def test_align_invariants(bs):
         k = real.size
         assert np.all(seg[:k] >= 0) and np.all(seg[k:] == -1)
     assert np.all(block_expert[total // bs:] == -1)
+
+
+def test_align_capacity_closed_form_and_tight():
+    # N slots over E_local experts padded to blocks of B: at most N + E_local*(B-1)
+    # rows and ceil(N/B) + E_local blocks
+    assert oracle.route_align_capacity(10, 3, 4) == (19, 6)
+    assert oracle.route_align_capacity(0, 5, 8) == (35, 5)
+    # reached exactly when every expert holds one route: E_local slots, each
+    # padded to a full block
+    El, B = 5, 4
+    ids = np.arange(El, dtype=np.int32).reshape(1, El)
+    poff, sorted_slots, block_expert, s2r = oracle.route_align(ids, None, El, B)
+    assert poff[-1] == El * B == oracle.route_align_capacity(El, El, B)[0]
+    assert len(sorted_slots) == oracle.route_align_capacity(El, El, B)[0]

@@ -175,3 +175,33 @@ def test_layer_all_remote_is_exact_zero():
     res = oracle.moe_layer(c)
     assert res["offsets"][-1] == 0
     assert np.all(res["out"] == 0.0)
+
+
+def test_ffn_rows_closed_form_and_row_independence():
+    # H = 2, F = 1: gate row (1, 0), up row (0, 1), W2 = [[2], [-1]]:
+    # y = silu(x0) * x1 * (2, -1) for each row, written out by hand
+    w1 = np.array([[1.0, 0.0], [0.0, 1.0]])
+    w2 = np.array([[2.0], [-1.0]])
+    x = np.array([[2.0, 3.0], [0.0, 5.0], [-1.0, -2.0]])
+    s = lambda v: v / (1.0 + math.exp(-v))
+    want = np.array([[2 * s(2.0) * 3.0, -s(2.0) * 3.0], [0.0, 0.0], [2 * s(-1.0) * -2.0, -s(-1.0) * -2.0]])
+    got = oracle.ffn_rows(x, w1, w2)
+    assert np.allclose(got, want, rtol=0, atol=1e-15)
+    # a row's result does not depend on the other rows
+    assert np.array_equal(oracle.ffn_rows(x[1:2], w1, w2)[0], got[1])
+
+
+def test_decode_weights_selects_the_storage_format():
+    # MXFP4: byte 0x21 holds element 0 in its low nibble (code 1 = 0.5) and
+    # element 1 in its high nibble (code 2 = 1.0); e8m0 128 scales by 2
+    codes = np.zeros((2, 1, 16), dtype=np.uint8)
+    codes[1, 0, 0] = 0x21
+    scales = np.full((2, 1, 1), 127, dtype=np.uint8)
+    scales[1, 0, 0] = 128
+    d = oracle.decode_weights(codes, scales, "mxfp4", 1)
+    assert d.shape == (1, 32) and d[0, 0] == 1.0 and d[0, 1] == 2.0 and not d[0, 2:].any()
+    # bf16 bits 0x3FC0 = 1.5, 0xC000 = -2; f32 passes through
+    bits = np.array([[[0x3FC0, 0xC000]]], dtype=np.uint16)
+    assert np.array_equal(oracle.decode_weights(bits, None, "bf16", 0), [[1.5, -2.0]])
+    f = np.array([[[0.25, -3.0]]], dtype=np.float32)
+    assert np.array_equal(oracle.decode_weights(f, None, "f32", 0), [[0.25, -3.0]])
