@@ -30,6 +30,10 @@
 //                value and its up value and silu(g)*u is formed in registers
 //   GEMM2        A rows are act rows; 256 output columns per tile
 //   rows         32-row MFMA blocks past the tile's last valid row are skipped
+//   epilogue     the weight fragment is the MFMA's first operand, so a lane
+//                holds 4 consecutive output columns of one row; bf16 results
+//                pass through a 2 KB LDS block per wave (beside the ring) and
+//                leave as 16 contiguous bytes per lane
 //
 // One expert's whole row set usually fits one M-tile (BM = 320 >= the
 // typical 256 +- 3 sigma rows at top-8 of 128), so each (expert, N-tile)
@@ -45,6 +49,7 @@ constexpr int kBN = kPanelRows; // weight rows per block
 constexpr int kStages = 4;      // LDS ring: steps k+1, k+2 in flight while step k computes
 constexpr int kRowBytes = kBK * 2;
 constexpr int kGrid = 256;       // persistent blocks: one per compute unit
+constexpr int kEpiBytes = 2048;  // per-wave LDS block of the epilogue: 32 rows x 64 bytes
 // cache policy of the weight loads: non-temporal (each weight panel is read
 // by one block, once), so the streamed weights do not push the re-read A
 // rows out of the caches
@@ -244,8 +249,8 @@ __device__ __forceinline__ void tile_kloop(const Tile& cur, const Tile& nxt, __a
     for (int mb = 0; mb < LIVE; ++mb) a[1][mb] = *reinterpret_cast<const bf16x8*>(base + a_addr[mb][1]);
 #pragma unroll
     for (int mb = 0; mb < LIVE; ++mb) {
-      acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][mb], b[0][0], acc[mb][0], 0, 0, 0);
-      acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][mb], b[0][1], acc[mb][1], 0, 0, 0);
+      acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[0][0], a[0][mb], acc[mb][0], 0, 0, 0);
+      acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[0][1], a[0][mb], acc[mb][1], 0, 0, 0);
     }
     // scheduling groups (mask 0x008: MFMA, 0x100: LDS read)
 #pragma unroll
@@ -257,8 +262,8 @@ __device__ __forceinline__ void tile_kloop(const Tile& cur, const Tile& nxt, __a
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int mb = 0; mb < LIVE; ++mb) {
-      acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][mb], b[1][0], acc[mb][0], 0, 0, 0);
-      acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][mb], b[1][1], acc[mb][1], 0, 0, 0);
+      acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[1][0], a[1][mb], acc[mb][0], 0, 0, 0);
+      acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[1][1], a[1][mb], acc[mb][1], 0, 0, 0);
     }
   };
   for (int kt = 0; kt < KT; ++kt, ++g) {
@@ -292,7 +297,8 @@ __global__ __launch_bounds__(kTThreads) void ffn_tiled_kernel(
   using U = Units<MBW>;
   constexpr int BM = U::BM;
   constexpr int RING = kStages * (BM + kBN) * kRowBytes;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[RING];
+  static_assert(RING + (kTThreads / 64) * kEpiBytes <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[RING + (kTThreads / 64) * kEpiBytes];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: resource choices stay scalar
@@ -331,7 +337,6 @@ __global__ __launch_bounds__(kTThreads) void ffn_tiled_kernel(
     }
   }
 
-  const int cl = lane & 31;
   int g = 0;
   while (true) {
     f32x16 acc[MBW][2];
@@ -353,29 +358,54 @@ __global__ __launch_bounds__(kTThreads) void ffn_tiled_kernel(
       default: tile_kloop<MBW, MBW, PACKED>(cur, nxt, ra, rz, lds, acc, KT, g, wave, lane, wm, wn); break;
     }
 
-    // Epilogue, straight from the accumulators (the LDS ring already holds
-    // the next tile's first steps).  acc[mb][nb][j] is C[row (j/4)*8 +
-    // (lane/32)*4 + j%4][col lane%32] of block b = 2*mb + wm; for each j the
-    // 32 lanes of a half-wave store 32 consecutive columns of one row.
+    // Epilogue (the LDS ring already holds the next tile's first steps).  The
+    // weight fragment is the MFMA's first operand, so acc[mb][nb][4q + i] is
+    // C[row lane%32 of block b = 2*mb + wm][column 8q + 4*(lane/32) + i of
+    // the 32-column block nb]: four consecutive columns per lane.  bf16
+    // results are packed to 8 bytes, written to this wave's own LDS block
+    // (row m at 64 m bytes, its four 16-byte pieces XOR-swizzled by m/4) and
+    // read back as 16 bytes of one row per lane, so each store instruction
+    // writes 16 rows x 64 contiguous bytes.  f32 results are stored as 16
+    // bytes per lane straight from the accumulators.
+    {
+      const int m = lane & 31, h = lane >> 5;
+      uint8_t* stage = lds + RING + wave * kEpiBytes;
 #pragma unroll
-    for (int mb = 0; mb < MBW; ++mb) {
-      if (mb >= live) continue;
+      for (int mb = 0; mb < MBW; ++mb) {
+        if (mb >= live) continue;
+        const int rb = (2 * mb + wm) * 32;  // the block's first row in the tile
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int r = (2 * mb + wm) * 32 + (j >> 2) * 8 + (lane >> 5) * 4 + (j & 3);
-        if (r >= cur.nrows) continue;
-        const int64_t orow = (int64_t)(cur.row0 + r) * ldo;
-        if constexpr (GATED) {
-          const float gt = acc[mb][0][j], u = acc[mb][1][j];
-          reinterpret_cast<uint16_t*>(out)[orow + cur.n0 + wn * 32 + cl] =
-              f32_to_bf16_bits(silu_fast(gt) * u);
-        } else if constexpr (sizeof(OT) == 2) {
+        for (int ob = 0; ob < (GATED ? 1 : 2); ++ob) {
+          const int col0 = cur.n0 + (GATED ? wn * 32 : wn * 64 + ob * 32);
+          if constexpr (!GATED && sizeof(OT) == 4) {
+            if (rb + m < cur.nrows) {
+              float* orow = reinterpret_cast<float*>(out) + (int64_t)(cur.row0 + rb + m) * ldo + col0 + 4 * h;
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
-            reinterpret_cast<uint16_t*>(out)[orow + cur.n0 + wn * 64 + nb * 32 + cl] = f32_to_bf16_bits(acc[mb][nb][j]);
-        } else {
+              for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<f32x4*>(orow + 8 * q) =
+                    f32x4{acc[mb][ob][4 * q], acc[mb][ob][4 * q + 1], acc[mb][ob][4 * q + 2], acc[mb][ob][4 * q + 3]};
+            }
+          } else {
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) out[orow + cur.n0 + wn * 64 + nb * 32 + cl] = acc[mb][nb][j];
+            for (int q = 0; q < 4; ++q) {
+              float v[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                if constexpr (GATED) v[i] = silu_fast(acc[mb][0][4 * q + i]) * acc[mb][1][4 * q + i];
+                else v[i] = acc[mb][ob][4 * q + i];
+              }
+              *reinterpret_cast<u32x2*>(stage + m * 64 + ((q ^ ((m >> 2) & 3)) * 16) + h * 8) =
+                  u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+              const int r = i * 16 + (lane >> 2), c = lane & 3;
+              const u32x4 w = *reinterpret_cast<const u32x4*>(stage + r * 64 + ((c ^ ((r >> 2) & 3)) * 16));
+              if (rb + r < cur.nrows)
+                *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + (int64_t)(cur.row0 + rb + r) * ldo + col0 +
+                                          c * 8) = w;
+            }
+          }
         }
       }
     }
