@@ -106,3 +106,28 @@ def test_tiled_rejects_unsupported_shapes():
     r2s = torch.full((8,), -1, dtype=torch.int32, device=DEV)
     with pytest.raises(moe.MoeError):
         moe.moe_grouped_ffn(x, 2, w1, w2, counts, offsets, r2s, tiled=True)
+
+
+@pytest.mark.parametrize("T,E,K", [(1024, 16, 4), (1000, 8, 4)])
+def test_tiled_f32_y_rounds_to_the_bf16_y(T, E, K):
+    # The tiled epilogue stores f32 y straight from the accumulators and bf16
+    # y through the per-wave LDS block: the f32 result rounded to bf16 must
+    # equal the bf16 result bit for bit, and both match the oracle.  T=1000
+    # leaves experts with row counts off the 32-row MFMA blocks (ragged
+    # last blocks, rows masked in the store).
+    H, F = 256, 128
+    c = synth.prefill_layer(seed=T + E, T=T, E=E, K=K, H=H, F=F)
+    d = case_to_device(c)
+    print(f"[tiled] f32 y T={T} E={E} K={K}", flush=True)
+    (tw, tid, tei), (counts, offsets, s2r, r2s) = moe.moe_topk_compact(d["logits"], K, c.renormalize, "softmax",
+                                                                       None, E)
+    t1, t2 = moe.moe_pack_ffn_weights(d["w1"], d["w2"])
+    yb = moe.moe_grouped_ffn(d["x"], K, t1, t2, counts, offsets, r2s, tiled=True)
+    yf = moe.moe_grouped_ffn(d["x"], K, t1, t2, counts, offsets, r2s, tiled=True, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.moe_layer(c)
+    R = int(ref["offsets"][-1])
+    assert int(offsets[-1].item()) == R
+    assert np.any(ref["counts"] % 32 != 0)
+    assert torch.equal(yf[:R].to(torch.bfloat16), yb[:R])
+    assert rel_max_err(host_f64(yf[:R]), ref["y"]) <= 1e-2
