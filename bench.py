@@ -65,7 +65,8 @@ def parse():
                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exit")
     p.add_argument("--profile", default="", metavar="WHAT",
                    help="only run one secondary for a kernel trace and exit: 'gate' (the five gate "
-                        "configurations) or 'decode:PATTERN' (one decode route pattern, every path)")
+                        "configurations), 'decode:PATTERN' (one decode route pattern, every path) or "
+                        "'mxfp4[:T<n>_<routes>]' (the MXFP4 weight-streaming cases)")
     return p.parse_args()
 
 
@@ -445,6 +446,95 @@ def bench_decode(dev, reps, only=None):
 
 
 # ---------------------------------------------------------------------------
+# secondary: MXFP4 experts (weight streaming at T = 2, 16, 64)
+
+
+def bench_mxfp4(dev, reps, only=None):
+    import numpy as np
+    import torch
+
+    import mixture_experts_routing_amd as moe
+    import synth
+
+    T_LIST, K, Eg, El, H, F = (2, 16, 64), 8, 256, 32, 4096, 2048
+    log("[bench] mxfp4: generating 32 experts (e2m1 codes + e8m0 scales, 0.43 GB)")
+    w1h, w1sh, w2h, w2sh = synth.mxfp4_weights(0, El, H, F)
+    u8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    w1, w1s, w2, w2s = u8(w1h), u8(w1sh), u8(w2h), u8(w2sh)
+    del w1h, w1sh, w2h, w2sh
+    # bytes one expert's weights occupy: codes (2 per byte) + one scale byte per 32
+    per_expert = (2 * F * H + H * F) // 2 + (2 * F * H + H * F) // 32
+    emap = synth.contiguous_expert_map(Eg, El)
+    emap_d = i32_dev(emap, dev)
+    inv = np.flatnonzero(emap >= 0)
+    nvar = 8  # rotated copies of the routes: consecutive calls touch different experts
+    res = {}
+    for routes in ("uniform", "all_local"):
+        for T in T_LIST:
+            name = f"T{T}_{routes}"
+            if only is not None and name != only:
+                continue
+            base = synth.mxfp4_case(T, routes, seed=0, with_weights=False)
+            x = bf16_dev(base.x, dev)
+            tw = f32_dev(base.topk_weights, dev)
+            loc = emap[base.topk_ids]
+            variants, n_exp = [], []
+            for v in range(nvar):
+                ids = np.where(loc >= 0, inv[(np.maximum(loc, 0) + 5 * v) % El], base.topk_ids).astype(np.int32)
+                variants.append(i32_dev(ids, dev))
+                n_exp.append(len(set(((loc[loc >= 0] + 5 * v) % El).tolist())))
+            N = T * K
+            outs = [(torch.empty(El, dtype=torch.int32, device=dev), torch.empty(El + 1, dtype=torch.int32, device=dev),
+                     torch.empty(N, dtype=torch.int32, device=dev), torch.empty(N, dtype=torch.int32, device=dev))
+                    for _ in range(nvar)]
+            fws = torch.empty(max(moe.grouped_ffn_workspace_bytes(T, K, H, F, El, moe.MOE_MXFP4), 16),
+                              dtype=torch.uint8, device=dev)
+            y = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
+            out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+            def compact(v):
+                moe.moe_route_compact(variants[v], emap_d, El, E_global=Eg, out=outs[v])
+
+            def ffn(v):
+                counts, offsets, _, r2s = outs[v]
+                moe.moe_grouped_ffn(x, K, w1, w2, counts, offsets, r2s, w1_scale=w1s, w2_scale=w2s, y=y,
+                                    workspace=fws)
+
+            def combine(v):
+                moe.moe_combine(y, tw, outs[v][2], out=out)
+
+            def each(*fns):
+                def run():
+                    for v in range(nvar):
+                        for f in fns:
+                            f(v)
+                return run
+
+            # the routes of every variant first (the FFN timing below reads
+            # them), checked on the host before any FFN launch
+            each(compact)()
+            torch.cuda.synchronize(dev)
+            for v in range(nvar):
+                c_, o_, _, r_ = (t.cpu().numpy() for t in outs[v])
+                R = int(o_[El])
+                assert R == int((loc >= 0).sum()) == int(c_.sum()) and np.all(np.diff(o_) == c_) and o_[0] == 0
+                assert np.all((r_[:R] >= 0) & (r_[:R] < N))
+            t_ffn = graph_ms(each(ffn), reps, dev) / nvar
+            t_layer = graph_ms(each(compact, ffn, combine), reps, dev) / nvar
+            wbytes = float(np.mean(n_exp)) * per_expert
+            d = {"T": T, "routes": routes, "local_slots": int((loc >= 0).sum()),
+                 "local_experts_mean": round(float(np.mean(n_exp)), 2), "layer_ms": round(t_layer, 4),
+                 "ffn_ms": round(t_ffn, 4), "tokens_per_s": round(T / (t_layer / 1e3), 1),
+                 "weight_bytes_mean": int(wbytes)}
+            if wbytes:
+                gbs = wbytes / (t_ffn / 1e3) / 1e9
+                d.update({"ffn_weight_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+            res[name] = d
+            log(f"[bench] mxfp4 {name}: " + json.dumps(d))
+    return res
+
+
+# ---------------------------------------------------------------------------
 # secondary: block-aligned layout (moe_route_align)
 
 
@@ -532,6 +622,8 @@ def main():
             res += [bench_gate(dev, E, 64, "sigmoid") for E in (128, 160, 256)]
         elif args.profile.startswith("decode:"):
             res = bench_decode(dev, 5, only=args.profile.split(":", 1)[1])
+        elif args.profile == "mxfp4" or args.profile.startswith("mxfp4:"):
+            res = bench_mxfp4(dev, 5, only=args.profile.split(":", 1)[1] if ":" in args.profile else None)
         else:
             raise SystemExit(f"unknown --profile {args.profile!r}")
         print(json.dumps({"profile": args.profile, "result": res}), flush=True)
@@ -546,6 +638,7 @@ def main():
             log(f"[bench] gate {g['scoring']} E={g['E']}: {g['ms'] * 1e3:.2f} us, {g['mrows_per_s']} Mrows/s, "
                 f"{g['gbs']} GB/s ({100 * g['hbm_frac']:.1f}% of HBM)")
         secondary["decode"] = bench_decode(dev, 5 if args.quick else 20)
+        secondary["mxfp4"] = bench_mxfp4(dev, 5 if args.quick else 20)
         secondary["route_align"] = bench_align(dev, 5 if args.quick else 20)
         for a in secondary["route_align"]:
             log(f"[bench] route_align {a['workload']} (T={a['T']}, K={a['K']}, E_local={a['E_local']}, "
