@@ -499,6 +499,39 @@ __device__ __forceinline__ bf16x8 widen_mx8(uint32_t w, uint32_t e8) {
   return bf16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
+// MXFP4 K units in batches of four for the decode kernels.  Within a batch
+// [u, u+4) the lanes of group g take unit u+g whole -- its 16 code bytes in
+// one load and its one scale byte -- and feed its 32 elements to the batch's
+// four MFMAs, 8 per MFMA (MFMA j: elements 8j..8j+7 of every group's unit).
+// The x (or act) operand takes the same elements, so each K element meets its
+// weight exactly once; only the order of the sum differs from unit by unit.
+// The weight loads of all NB batches are issued before the first MFMA, so a
+// wave keeps 1 KB of codes per batch in flight (up to 8 KB).
+template <int NB>
+__device__ __forceinline__ void mx_batches(f32x4& acc, const uint16_t* __restrict__ xr,
+                                           const uint8_t* __restrict__ wrow, const uint8_t* __restrict__ srow, int u,
+                                           int g) {
+  u32x4 cw[NB];
+  uint32_t sc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    cw[b] = *reinterpret_cast<const u32x4*>(wrow + 16 * (u + 4 * b + g));
+    sc[b] = srow[u + 4 * b + g];
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const uint16_t* xp = xr + 32 * (u + 4 * b + g);
+    bf16x8 xa[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xa[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xp + 8 * j));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j], widen_mx8(cw[b][j], sc[b]), acc, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);  // the next batch's x loads stay after these MFMAs
+  }
+}
+
+
 __device__ __forceinline__ bf16x8 unit_bf16(const uint16_t* __restrict__ row, int u, int g) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + 32 * u + 8 * g));
 }
@@ -606,15 +639,33 @@ __global__ __launch_bounds__(kDecThreads) void ffn1_decode_kernel(
       // W1 row of this lane's MFMA column: gate row (c < 8) or up row
       const int64_t rw = (int64_t)e * 2 * F + (c >> 3) * F + cg * 8 + (c & 7);
       int u = u_begin;
-      for (; u + U <= u_end; u += U) {
-        WUnit<MX> b[U];
-        bf16x8 a[U];
+      if constexpr (MX) {
+        const uint8_t* wrow = static_cast<const uint8_t*>(w1) + rw * (H / 2);
+        const uint8_t* srow = w1s + rw * (H / 32);
+        for (; u + 32 <= u_end; u += 32) mx_batches<8>(acc, xr, wrow, srow, u, g);
+        if (u + 16 <= u_end) {
+          mx_batches<4>(acc, xr, wrow, srow, u, g);
+          u += 16;
+        }
+        if (u + 8 <= u_end) {
+          mx_batches<2>(acc, xr, wrow, srow, u, g);
+          u += 8;
+        }
+        if (u + 4 <= u_end) {
+          mx_batches<1>(acc, xr, wrow, srow, u, g);
+          u += 4;
+        }
+      } else {
+        for (; u + U <= u_end; u += U) {
+          WUnit<MX> b[U];
+          bf16x8 a[U];
 #pragma unroll
-        for (int j = 0; j < U; ++j) b[j].load(w1, w1s, rw, H, u + j, g);
+          for (int j = 0; j < U; ++j) b[j].load(w1, w1s, rw, H, u + j, g);
 #pragma unroll
-        for (int j = 0; j < U; ++j) a[j] = unit_bf16(xr, u + j, g);
+          for (int j = 0; j < U; ++j) a[j] = unit_bf16(xr, u + j, g);
 #pragma unroll
-        for (int j = 0; j < U; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], b[j].get(), acc, 0, 0, 0);
+          for (int j = 0; j < U; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], b[j].get(), acc, 0, 0, 0);
+        }
       }
       for (; u < u_end; ++u) {
         WUnit<MX> b;
@@ -679,15 +730,33 @@ __global__ __launch_bounds__(kDecThreads) void ffn2_decode_kernel(
       const uint16_t* ar = act + (int64_t)(row0 + (c < nrows ? c : 0)) * F;
       const int64_t rw = (int64_t)e * H + cg * 16 + c;
       int u = u_begin;
-      for (; u + kDecUnroll <= u_end; u += kDecUnroll) {
-        WUnit<MX> b[kDecUnroll];
-        bf16x8 a[kDecUnroll];
+      if constexpr (MX) {
+        const uint8_t* wrow = static_cast<const uint8_t*>(w2) + rw * (F / 2);
+        const uint8_t* srow = w2s + rw * (F / 32);
+        for (; u + 32 <= u_end; u += 32) mx_batches<8>(acc, ar, wrow, srow, u, g);
+        if (u + 16 <= u_end) {
+          mx_batches<4>(acc, ar, wrow, srow, u, g);
+          u += 16;
+        }
+        if (u + 8 <= u_end) {
+          mx_batches<2>(acc, ar, wrow, srow, u, g);
+          u += 8;
+        }
+        if (u + 4 <= u_end) {
+          mx_batches<1>(acc, ar, wrow, srow, u, g);
+          u += 4;
+        }
+      } else {
+        for (; u + kDecUnroll <= u_end; u += kDecUnroll) {
+          WUnit<MX> b[kDecUnroll];
+          bf16x8 a[kDecUnroll];
 #pragma unroll
-        for (int j = 0; j < kDecUnroll; ++j) b[j].load(w2, w2s, rw, F, u + j, g);
+          for (int j = 0; j < kDecUnroll; ++j) b[j].load(w2, w2s, rw, F, u + j, g);
 #pragma unroll
-        for (int j = 0; j < kDecUnroll; ++j) a[j] = unit_bf16(ar, u + j, g);
+          for (int j = 0; j < kDecUnroll; ++j) a[j] = unit_bf16(ar, u + j, g);
 #pragma unroll
-        for (int j = 0; j < kDecUnroll; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], b[j].get(), acc, 0, 0, 0);
+          for (int j = 0; j < kDecUnroll; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], b[j].get(), acc, 0, 0, 0);
+        }
       }
       for (; u < u_end; ++u) {
         WUnit<MX> b;
