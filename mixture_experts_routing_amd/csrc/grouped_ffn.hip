@@ -532,6 +532,8 @@ __device__ __forceinline__ void mx_batches(f32x4& acc, const uint16_t* __restric
 }
 
 
+
+
 __device__ __forceinline__ bf16x8 unit_bf16(const uint16_t* __restrict__ row, int u, int g) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + 32 * u + 8 * g));
 }
@@ -559,6 +561,93 @@ struct WUnit<true> {
   }
   __device__ __forceinline__ bf16x8 get() const { return widen_mx8(c, e8); }
 };
+
+// Workgroup barrier that orders LDS accesses only: global loads in flight
+// stay in flight across it (a full __syncthreads waits for them too).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// One wave's share of a decode item: the dot products of the 16 A rows (xr:
+// this lane's row, bf16) with the 16 weight rows (rw: this lane's row) over K
+// units [u, u_end).  xr may point into LDS (staged rows) or global memory.
+template <bool MX, int U>
+__device__ __forceinline__ f32x4 tile_dot(const uint16_t* __restrict__ xr, const void* __restrict__ w,
+                                          const uint8_t* __restrict__ ws, int64_t rw, int kdim, int u, int u_end,
+                                          int g) {
+  f32x4 acc = {0, 0, 0, 0};
+  if constexpr (MX) {
+    const uint8_t* wrow = static_cast<const uint8_t*>(w) + rw * (kdim / 2);
+    const uint8_t* srow = ws + rw * (kdim / 32);
+    for (; u + 32 <= u_end; u += 32) mx_batches<8>(acc, xr, wrow, srow, u, g);
+    if (u + 16 <= u_end) {
+      mx_batches<4>(acc, xr, wrow, srow, u, g);
+      u += 16;
+    }
+    if (u + 8 <= u_end) {
+      mx_batches<2>(acc, xr, wrow, srow, u, g);
+      u += 8;
+    }
+    if (u + 4 <= u_end) {
+      mx_batches<1>(acc, xr, wrow, srow, u, g);
+      u += 4;
+    }
+  } else {
+    for (; u + U <= u_end; u += U) {
+      WUnit<MX> b[U];
+      bf16x8 a[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j) b[j].load(w, ws, rw, kdim, u + j, g);
+#pragma unroll
+      for (int j = 0; j < U; ++j) a[j] = unit_bf16(xr, u + j, g);
+#pragma unroll
+      for (int j = 0; j < U; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], b[j].get(), acc, 0, 0, 0);
+    }
+  }
+  for (; u < u_end; ++u) {
+    WUnit<MX> b;
+    b.load(w, ws, rw, kdim, u, g);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unit_bf16(xr, u, g), b.get(), acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// Staged A rows of a decode item.  When the splits leave several waves of a
+// block on the same K range, those waves would each load the same 16 A rows
+// from global memory; instead the block copies the item's distinct rows (at
+// most 16, rows past the tile's end use row 0) into LDS once, with
+// contiguous 16-byte loads, and every wave reads its fragments from there.
+// The copy and its two barriers pay off with at least 4 waves per range
+// (S <= 4), or 2 per range (S = 8) when the tile holds 8 rows or more.  Only
+// the MXFP4 kernels stage: their A rows are 4x the bytes of the weight codes
+// they meet, and the 128 KB block they need keeps a kernel's blocks from
+// sharing a compute unit with the previous kernel's, which costs the bf16
+// decode kernels more than the staging saves them.
+// Row r sits at r * (2 K + kXsPad) bytes: rows start 16 bytes apart modulo
+// the 256-byte bank period, so the 16 lanes of a quarter-wave (16 rows, one
+// piece) hit distinct banks.
+constexpr int kXsMaxK = 4096;  // longest reduction whose rows are staged
+
+__device__ __forceinline__ bool stage_item(int S, int nrows) { return S <= 4 || (S <= 8 && nrows >= 8); }
+constexpr int kXsPad = 16;
+constexpr int kXsBytes = 16 * (2 * kXsMaxK + kXsPad);
+
+// Copy rows [0, n) of an item (row r from src_row(r), K elements each) into
+// xs, then a barrier (the rows are visible).  Every thread of the block takes
+// part; the caller has passed a barrier after the previous item's reads.
+template <typename SrcRow>
+__device__ __forceinline__ void stage_rows(uint8_t* __restrict__ xs, int n, int kdim, SrcRow src_row) {
+  const int ppr = kdim / 8;  // 16-byte pieces per row
+  const int RS = 2 * kdim + kXsPad;
+  for (int p = threadIdx.x; p < n * ppr; p += kDecThreads) {
+    const int r = p / ppr, q = p - r * ppr;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(src_row(r) + 8 * q);
+    *reinterpret_cast<u32x4*>(xs + r * RS + 16 * q) = v;
+  }
+  lds_barrier();
+}
 
 // Compaction inputs and outputs of the fused GEMM1 (ROUTES = true): every
 // wave derives the route table itself from topk_ids and the expert map, and
@@ -588,6 +677,8 @@ __global__ __launch_bounds__(kDecThreads) void ffn1_decode_kernel(
     const int32_t* __restrict__ r2s, uint16_t* __restrict__ act, FusedRoutes fr) {
   constexpr int U = dec_unroll1<MX>();
   __shared__ float red[kDecWaves][4][64];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[MX ? kXsBytes : 16];
+  __shared__ int xtok[16];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
   const bool small = ROUTES || El <= 64;  // uniform
   TileTab tab{};
@@ -619,6 +710,7 @@ __global__ __launch_bounds__(kDecThreads) void ffn1_decode_kernel(
   const int ks = wave % S, cgl = wave / S;
   const int per = (units + S - 1) / S;
   const int u_begin = min(units, ks * per), u_end = min(units, u_begin + per);
+  const bool stage_ok = MX && H <= kXsMaxK;  // uniform
 
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
     const int tile = it / ipt, cb = it % ipt;
@@ -627,51 +719,30 @@ __global__ __launch_bounds__(kDecThreads) void ffn1_decode_kernel(
     else find_tile(counts, offsets, El, 16, tile, e, row0, nrows);
     const int cg = cb * cpb + cgl;
     const bool active = cg < CG;
+    // W1 row of this lane's MFMA column: gate row (c < 8) or up row
+    const int64_t rw = (int64_t)e * 2 * F + (c >> 3) * F + cg * 8 + (c & 7);
     f32x4 acc = {0, 0, 0, 0};
-    if (active) {
+    if (stage_ok && stage_item(S, nrows)) {  // uniform: one tile per item
+      const int n = nrows < 16 ? nrows : 16;
+      if (wave == 0) {  // the x row (token) of each of the item's rows
+        const int r = row0 + (lane < n ? lane : 0);
+        int slot;
+        if constexpr (ROUTES) slot = __shfl(inv, r, 64);
+        else slot = r2s[r];
+        if (lane < 16) xtok[lane] = slot / K;
+      }
+      lds_barrier();  // xtok visible; every wave is done with the previous item's rows
+      stage_rows(xs, n, H, [&](int r) { return x + (int64_t)xtok[r] * H; });
+      if (active)
+        acc = tile_dot<MX, U>(reinterpret_cast<const uint16_t*>(xs + (c < n ? c : 0) * (2 * H + kXsPad)), w1, w1s,
+                              rw, H, u_begin, u_end, g);
+    } else if (active) {
       // rows past the tile's end reuse the first row; their results are dropped
       const int r = row0 + (c < nrows ? c : 0);
       int slot;
       if constexpr (ROUTES) slot = __shfl(inv, r, 64);
       else slot = r2s[r];
-      const int tok = slot / K;
-      const uint16_t* xr = x + (int64_t)tok * H;
-      // W1 row of this lane's MFMA column: gate row (c < 8) or up row
-      const int64_t rw = (int64_t)e * 2 * F + (c >> 3) * F + cg * 8 + (c & 7);
-      int u = u_begin;
-      if constexpr (MX) {
-        const uint8_t* wrow = static_cast<const uint8_t*>(w1) + rw * (H / 2);
-        const uint8_t* srow = w1s + rw * (H / 32);
-        for (; u + 32 <= u_end; u += 32) mx_batches<8>(acc, xr, wrow, srow, u, g);
-        if (u + 16 <= u_end) {
-          mx_batches<4>(acc, xr, wrow, srow, u, g);
-          u += 16;
-        }
-        if (u + 8 <= u_end) {
-          mx_batches<2>(acc, xr, wrow, srow, u, g);
-          u += 8;
-        }
-        if (u + 4 <= u_end) {
-          mx_batches<1>(acc, xr, wrow, srow, u, g);
-          u += 4;
-        }
-      } else {
-        for (; u + U <= u_end; u += U) {
-          WUnit<MX> b[U];
-          bf16x8 a[U];
-#pragma unroll
-          for (int j = 0; j < U; ++j) b[j].load(w1, w1s, rw, H, u + j, g);
-#pragma unroll
-          for (int j = 0; j < U; ++j) a[j] = unit_bf16(xr, u + j, g);
-#pragma unroll
-          for (int j = 0; j < U; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], b[j].get(), acc, 0, 0, 0);
-        }
-      }
-      for (; u < u_end; ++u) {
-        WUnit<MX> b;
-        b.load(w1, w1s, rw, H, u, g);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unit_bf16(xr, u, g), b.get(), acc, 0, 0, 0);
-      }
+      acc = tile_dot<MX, U>(x + (int64_t)(slot / K) * H, w1, w1s, rw, H, u_begin, u_end, g);
     }
     if (S > 1) {
 #pragma unroll
@@ -704,6 +775,7 @@ __global__ __launch_bounds__(kDecThreads) void ffn2_decode_kernel(
     const uint8_t* __restrict__ w2s, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     YT* __restrict__ y) {
   __shared__ float red[kDecWaves][4][64];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[MX ? kXsBytes : 16];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
   const bool small = El <= 64;  // uniform
   TileTab tab{};
@@ -717,6 +789,7 @@ __global__ __launch_bounds__(kDecThreads) void ffn2_decode_kernel(
   const int ks = wave % S, cgl = wave / S;
   const int per = (units + S - 1) / S;
   const int u_begin = min(units, ks * per), u_end = min(units, u_begin + per);
+  const bool stage_ok = MX && F <= kXsMaxK;  // uniform
 
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
     const int tile = it / ipt, cb = it % ipt;
@@ -725,44 +798,19 @@ __global__ __launch_bounds__(kDecThreads) void ffn2_decode_kernel(
     else find_tile(counts, offsets, El, 16, tile, e, row0, nrows);
     const int cg = cb * cpb + cgl;
     const bool active = cg < CG;
+    const int64_t rw = (int64_t)e * H + cg * 16 + c;
     f32x4 acc = {0, 0, 0, 0};
-    if (active) {
-      const uint16_t* ar = act + (int64_t)(row0 + (c < nrows ? c : 0)) * F;
-      const int64_t rw = (int64_t)e * H + cg * 16 + c;
-      int u = u_begin;
-      if constexpr (MX) {
-        const uint8_t* wrow = static_cast<const uint8_t*>(w2) + rw * (F / 2);
-        const uint8_t* srow = w2s + rw * (F / 32);
-        for (; u + 32 <= u_end; u += 32) mx_batches<8>(acc, ar, wrow, srow, u, g);
-        if (u + 16 <= u_end) {
-          mx_batches<4>(acc, ar, wrow, srow, u, g);
-          u += 16;
-        }
-        if (u + 8 <= u_end) {
-          mx_batches<2>(acc, ar, wrow, srow, u, g);
-          u += 8;
-        }
-        if (u + 4 <= u_end) {
-          mx_batches<1>(acc, ar, wrow, srow, u, g);
-          u += 4;
-        }
-      } else {
-        for (; u + kDecUnroll <= u_end; u += kDecUnroll) {
-          WUnit<MX> b[kDecUnroll];
-          bf16x8 a[kDecUnroll];
-#pragma unroll
-          for (int j = 0; j < kDecUnroll; ++j) b[j].load(w2, w2s, rw, F, u + j, g);
-#pragma unroll
-          for (int j = 0; j < kDecUnroll; ++j) a[j] = unit_bf16(ar, u + j, g);
-#pragma unroll
-          for (int j = 0; j < kDecUnroll; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], b[j].get(), acc, 0, 0, 0);
-        }
-      }
-      for (; u < u_end; ++u) {
-        WUnit<MX> b;
-        b.load(w2, w2s, rw, F, u, g);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unit_bf16(ar, u, g), b.get(), acc, 0, 0, 0);
-      }
+    if (stage_ok && stage_item(S, nrows)) {  // uniform: one tile per item
+      const int n = nrows < 16 ? nrows : 16;
+      lds_barrier();  // every wave is done with the previous item's rows
+      stage_rows(xs, n, F, [&](int r) { return act + (int64_t)(row0 + r) * F; });
+      if (active)
+        acc = tile_dot<MX, kDecUnroll>(reinterpret_cast<const uint16_t*>(xs + (c < n ? c : 0) * (2 * F + kXsPad)), w2,
+                                       w2s, rw, F, u_begin, u_end, g);
+    } else if (active) {
+      // rows past the tile's end reuse the first row; their results are dropped
+      acc = tile_dot<MX, kDecUnroll>(act + (int64_t)(row0 + (c < nrows ? c : 0)) * F, w2, w2s, rw, F, u_begin, u_end,
+                                     g);
     }
     if (S > 1) {
 #pragma unroll
