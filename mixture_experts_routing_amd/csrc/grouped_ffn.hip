@@ -625,14 +625,15 @@ __device__ __forceinline__ f32x4 tile_dot(const uint16_t* __restrict__ xr, const
 // they meet, and the 128 KB block they need keeps a kernel's blocks from
 // sharing a compute unit with the previous kernel's, which costs the bf16
 // decode kernels more than the staging saves them.
-// Row r sits at r * (2 K + kXsPad) bytes: rows start 16 bytes apart modulo
-// the 256-byte bank period, so the 16 lanes of a quarter-wave (16 rows, one
+// Row r sits at r * (2 K + kXsPad) bytes, an odd multiple of 16 (K is a
+// multiple of 32), so the 16 rows start in 16 distinct 16-byte slots of the
+// 256-byte bank period and the 16 lanes of a quarter-wave (16 rows, one
 // piece) hit distinct banks.
 constexpr int kXsMaxK = 4096;  // longest reduction whose rows are staged
-
-__device__ __forceinline__ bool stage_item(int S, int nrows) { return S <= 4 || (S <= 8 && nrows >= 8); }
 constexpr int kXsPad = 16;
 constexpr int kXsBytes = 16 * (2 * kXsMaxK + kXsPad);
+
+__device__ __forceinline__ bool stage_item(int S, int nrows) { return S <= 4 || (S <= 8 && nrows >= 8); }
 
 // Copy rows [0, n) of an item (row r from src_row(r), K elements each) into
 // xs, then a barrier (the rows are visible).  Every thread of the block takes
