@@ -896,6 +896,42 @@ struct TileOperands {
   }
 };
 
+// MXFP4: the batch layout of mx_batches for the (at most) four units
+// [u0, u0 + n) of a wave: the lanes of group g hold unit u0 + g whole; a
+// group past the wave's range (g >= n) loads a valid unit and feeds zeros.
+template <>
+struct TileOperands<true> {
+  u32x4 cw;                // the 16 code bytes of this lane group's unit
+  uint32_t sc;             // its scale byte
+  bf16x8 a[kFusedUnits];   // its act elements, 8 per MFMA
+  int row0, nrows;
+
+  __device__ __forceinline__ void load(const TileTab& tab, int tile, const uint16_t* __restrict__ act,
+                                       const void* __restrict__ w2, const uint8_t* __restrict__ w2s, int H, int F,
+                                       int cg, int u0, int units, int c, int g) {
+    int e = 0;
+    tab_find(tab, 16, tile, e, row0, nrows);
+    const uint16_t* ar = act + (int64_t)(row0 + (c < nrows ? c : 0)) * F;
+    const int64_t rw = (int64_t)e * H + cg * 16 + c;
+    const int u = min(u0 + g, units - 1);
+    cw = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(w2) + rw * (F / 2) + 16 * u);
+    sc = w2s[rw * (F / 32) + u];
+#pragma unroll
+    for (int j = 0; j < kFusedUnits; ++j) a[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ar + 32 * u + 8 * j));
+  }
+
+  __device__ __forceinline__ f32x4 mma(int n) const {
+    const bool live = ((int)(threadIdx.x & 63) >> 4) < n;
+    const bf16x8 zero = {};
+    f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < kFusedUnits; ++j)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(live ? a[j] : zero, live ? widen_mx8(cw[j], sc) : zero, acc, 0, 0,
+                                                    0);
+    return acc;
+  }
+};
+
 // GEMM2 with the combine in its tail.  Block b owns the 16 output columns
 // [16 cg, 16 cg + 16), cg = b, b + grid, ..., across every tile: the 16 waves
 // split the reduction 16 ways for one tile at a time, wave 0 adds the
@@ -963,27 +999,9 @@ __global__ __launch_bounds__(kDecThreads) void ffn2_combine_kernel(
       for (int tile = 0; tile < tiles; ++tile) {
         int e = 0, row0 = 0, nrows = 0;
         tab_find(tab, 16, tile, e, row0, nrows);
-        f32x4 acc = {0, 0, 0, 0};
         const uint16_t* ar = act + (int64_t)(row0 + (c < nrows ? c : 0)) * F;
         const int64_t rw = (int64_t)e * H + cg * 16 + c;
-        int u = u_begin;
-        for (; u + kDecUnroll <= u_end; u += kDecUnroll) {
-          WUnit<MX> b[kDecUnroll];
-          bf16x8 a[kDecUnroll];
-#pragma unroll
-          for (int j = 0; j < kDecUnroll; ++j) b[j].load(w2, w2s, rw, F, u + j, g);
-#pragma unroll
-          for (int j = 0; j < kDecUnroll; ++j) a[j] = unit_bf16(ar, u + j, g);
-#pragma unroll
-          for (int j = 0; j < kDecUnroll; ++j)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], b[j].get(), acc, 0, 0, 0);
-        }
-        for (; u < u_end; ++u) {
-          WUnit<MX> b;
-          b.load(w2, w2s, rw, F, u, g);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unit_bf16(ar, u, g), b.get(), acc, 0, 0, 0);
-        }
-        finish_tile(acc, row0, nrows);
+        finish_tile(tile_dot<MX, kDecUnroll>(ar, w2, w2s, rw, F, u_begin, u_end, g), row0, nrows);
       }
     }
     for (int i = threadIdx.x; i < T * 16; i += kDecThreads) {
