@@ -526,6 +526,15 @@ def bench_mxfp4(dev, reps, only=None):
                  "local_experts_mean": round(float(np.mean(n_exp)), 2), "layer_ms": round(t_layer, 4),
                  "ffn_ms": round(t_ffn, 4), "tokens_per_s": round(T / (t_layer / 1e3), 1),
                  "weight_bytes_mean": int(wbytes)}
+            if N <= 64:  # the boundary-fused layer (compaction in GEMM1, combine in GEMM2)
+                xws = torch.empty(max(moe.fused_experts_workspace_bytes(T, K, H, F, El, moe.MOE_MXFP4), 16),
+                                  dtype=torch.uint8, device=dev)
+
+                def fused(v):
+                    moe.moe_fused_experts(x, variants[v], tw, w1, w2, emap_d, Eg, w1_scale=w1s, w2_scale=w2s,
+                                          out=out, routes=outs[v], workspace=xws)
+
+                d["fused_layer_ms"] = round(graph_ms(each(fused), reps, dev) / nvar, 4)
             if wbytes:
                 gbs = wbytes / (t_ffn / 1e3) / 1e9
                 d.update({"ffn_weight_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
