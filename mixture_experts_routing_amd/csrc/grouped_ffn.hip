@@ -463,11 +463,15 @@ constexpr int kDecUnroll = 8;
 // time grows with the bytes it streams, below that the memory latency
 // dominates -- and `grid` persistent blocks take ceil(items / grid) rounds.
 // A split that leaves compute units idle (items just under a multiple of the
-// grid) loses to one that keeps them all streaming.  Ties go to the smaller
-// S (fewer partial sums to add).
-constexpr int kSplitLatencyUnits = 4;
+// grid) loses to one that keeps them all streaming.  Of two splits with the
+// same estimate the larger wins if it needs no more rounds (its extra items
+// land on otherwise idle compute units), else the smaller (fewer partial
+// sums to add).  The latency floor is in bytes: a unit is 1 KB of bf16
+// weights per wave but 256 bytes of MXFP4 codes.
+constexpr int kSplitLatencyUnits = 4;     // bf16
+constexpr int kSplitLatencyUnitsMX = 32;  // MXFP4
 
-__device__ __forceinline__ int decode_split(int tiles, int col_groups, int units, int grid) {
+__device__ __forceinline__ int decode_split(int tiles, int col_groups, int units, int grid, unsigned lat) {
   // The inputs are wave-uniform: make that visible so the search runs on the
   // scalar unit with 32-bit divisions (a few hundred cycles at most).
   tiles = __builtin_amdgcn_readfirstlane(tiles);
@@ -475,15 +479,17 @@ __device__ __forceinline__ int decode_split(int tiles, int col_groups, int units
   const unsigned g = (unsigned)grid;
   int best = 1;
   uint64_t best_cost = ~(uint64_t)0;
+  unsigned best_rounds = ~0u;
   for (int s = 1; s <= kDecWaves && s <= units; s <<= 1) {
     const unsigned cpb = (unsigned)(kDecWaves / s);
     const unsigned items = (unsigned)tiles * (((unsigned)col_groups + cpb - 1) / cpb);
     const unsigned rounds = (items + g - 1) / g;
     const unsigned per = ((unsigned)units + s - 1) / (unsigned)s;
-    const uint64_t cost = (uint64_t)rounds * (per > kSplitLatencyUnits ? per : (unsigned)kSplitLatencyUnits);
-    if (cost < best_cost) {
+    const uint64_t cost = (uint64_t)rounds * (per > lat ? per : lat);
+    if (cost < best_cost || (cost == best_cost && rounds <= best_rounds)) {
       best = s;
       best_cost = cost;
+      best_rounds = rounds;
     }
   }
   return best;
@@ -704,7 +710,7 @@ __global__ __launch_bounds__(kDecThreads) void ffn1_decode_kernel(
   }
   const int tiles = small ? tab.total : count_tiles(counts, El, 16);
   const int CG = F / 8, units = H / 32;  // column groups of 8 act columns
-  const int S = decode_split(tiles, CG, units, gridDim.x);
+  const int S = decode_split(tiles, CG, units, gridDim.x, MX ? kSplitLatencyUnitsMX : kSplitLatencyUnits);
   const int cpb = kDecWaves / S;         // column groups per item
   const int ipt = (CG + cpb - 1) / cpb;  // items per tile
   const int items = tiles * ipt;
@@ -783,7 +789,7 @@ __global__ __launch_bounds__(kDecThreads) void ffn2_decode_kernel(
   if (small) tab = load_tile_tab(counts, offsets, El, 16);
   const int tiles = small ? tab.total : count_tiles(counts, El, 16);
   const int CG = H / 16, units = F / 32;
-  const int S = decode_split(tiles, CG, units, gridDim.x);
+  const int S = decode_split(tiles, CG, units, gridDim.x, MX ? kSplitLatencyUnitsMX : kSplitLatencyUnits);
   const int cpb = kDecWaves / S;
   const int ipt = (CG + cpb - 1) / cpb;
   const int items = tiles * ipt;
