@@ -466,9 +466,9 @@ constexpr int kDecUnroll = 8;
 // grid) loses to one that keeps them all streaming.  Of two splits with the
 // same estimate the larger wins if it needs no more rounds (its extra items
 // land on otherwise idle compute units), else the smaller (fewer partial
-// sums to add).  The latency floor is in bytes: a unit is 1 KB of bf16
-// weights per wave but 256 bytes of MXFP4 codes.
-constexpr int kSplitLatencyUnits = 4;     // bf16
+// sums to add).  The latency floor is 8 KB of weights per wave: 8 units of
+// bf16 (1 KB per wave each), 32 of MXFP4 codes (256 bytes).
+constexpr int kSplitLatencyUnits = 8;     // bf16
 constexpr int kSplitLatencyUnitsMX = 32;  // MXFP4
 
 __device__ __forceinline__ int decode_split(int tiles, int col_groups, int units, int grid, unsigned lat) {
