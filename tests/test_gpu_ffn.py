@@ -146,13 +146,15 @@ def small_case(w_dtype, T, K, Eg, El, H, F, hot, seed, out_dtype="bf16"):
 
 
 @pytest.mark.parametrize("w_dtype", ["bf16", "mxfp4"])
-@pytest.mark.parametrize("H,F", [(96, 64), (256, 160), (512, 384), (1024, 4096), (1120, 160), (2080, 1056)])
+@pytest.mark.parametrize("H,F", [(96, 64), (256, 160), (512, 384), (1024, 4096), (1120, 160), (2080, 1056),
+                                 (4128, 96)])
 @pytest.mark.parametrize("T", [1, 3, 9])
 @pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
 def test_decode_split_k_shapes(w_dtype, H, F, T, out_dtype):
     # few rows per expert: the K dimension is split over the waves of a block
-    # and reduced in a fixed order; with 35, 65 or 33 K units (the last two
-    # shapes) the chosen splits leave uneven and empty K chunks
+    # and reduced in a fixed order; with 35, 65 or 33 K units (the 1120 and
+    # 2080 shapes) the chosen splits leave uneven and empty K chunks; H = 4128
+    # is past the longest MXFP4 A row staged in LDS (GEMM1 reads it directly)
     c = small_case(w_dtype, T, 4, 12, 6, H, F, hot=(T == 9), seed=H + F + T, out_dtype=out_dtype)
     res = run_layer(c)
     ref = oracle.moe_layer(c)

@@ -89,6 +89,27 @@ def test_fused_mxfp4(T, routes):
     check(c, case_to_device(c), "mxfp4")
 
 
+@pytest.mark.parametrize("H,F", [(256, 160), (256, 2080), (4128, 64)])
+def test_fused_mxfp4_uneven_units(H, F):
+    # MXFP4 GEMM2 operands in the batched layout with partial batches (5 K
+    # units over 16 waves: one each, the rest none), the unpipelined GEMM2
+    # (65 units: more than 4 per wave), and GEMM1 rows longer than the LDS
+    # staging holds (H = 4128)
+    T, K, Eg, El = 5, 4, 16, 6
+    rng = np.random.default_rng(H + F)
+    emap = synth.random_expert_map(Eg, El, seed=H + F)
+    ids = np.stack([rng.choice(Eg, size=K, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.dirichlet(np.ones(K), size=T).astype(np.float32)
+    c = synth.MoECase(name=f"mx_uneven_{H}_{F}", T=T, E_global=Eg, E_local=El, K=K, H=H, F=F, renormalize=False,
+                      x_dtype="bf16", w_dtype="mxfp4", out_dtype="bf16", x=synth.bf16_normal((T, H), 1.0, 9, 1),
+                      w1=rng.integers(0, 256, size=(El, 2 * F, H // 2), dtype=np.uint8),
+                      w2=rng.integers(0, 256, size=(El, H, F // 2), dtype=np.uint8),
+                      w1_scale=rng.integers(119, 128, size=(El, 2 * F, H // 32), dtype=np.uint8),
+                      w2_scale=rng.integers(119, 128, size=(El, H, F // 32), dtype=np.uint8),
+                      topk_ids=ids, topk_weights=w, expert_map=emap)
+    check(c, case_to_device(c), "mxfp4 uneven")
+
+
 def small_case(name, T, K, Eg, El, H, F, ids, seed, emap=None):
     rng = np.random.default_rng([seed, 77])
     w = rng.dirichlet(np.ones(K), size=T).astype(np.float32)
