@@ -130,18 +130,23 @@ constexpr int kCompactWaves = 16;
 constexpr int kCompactBlockSlots = kCompactWaves * 64;  // 1024
 constexpr int kCompactSingleMax = 4096;                 // one block handles up to this many slots
 
-// For the 64 lanes of a wave holding local ids l (-1 = remote/absent): the
-// number of lower lanes with the same id, and the number with that id.
-__device__ __forceinline__ void wave_group_rank(int l, int lane, int& below, int& total) {
-  below = 0;
-  total = 0;
-#pragma unroll 16
-  for (int j = 0; j < 64; ++j) {
-    const int lj = __builtin_amdgcn_readlane(l, j);
-    const int eq = (lj == l) ? 1 : 0;
-    total += eq;
-    below += (j < lane) ? eq : 0;
+// For the 64 lanes of a wave holding local ids l (-1 = remote/absent,
+// l < El): the number of lower lanes with the same id, and the number with
+// that id.  Lane j holds this lane's id exactly when every bit of l+1 agrees,
+// so the lanes of equal id are the AND over those bits of "the lanes where
+// the bit is set" (one ballot) or its complement: ceil(log2(El+1)) ballots.
+// Every lane of the wave must be active.
+__device__ __forceinline__ void wave_group_rank(int l, int El, int& below, int& total) {
+  const uint32_t u = (uint32_t)(l + 1);  // 0 .. El
+  const int nbits = El > 0 ? 32 - __clz(El) : 0;
+  uint64_t m = ~0ull;
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (u >> b) & 1u;
+    const uint64_t set = __ballot(bit);
+    m &= bit ? set : ~set;
   }
+  total = __popcll(m);
+  below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 // Per-expert exclusive prefix over the kCompactWaves rows of run[w*El + e]

@@ -11,8 +11,8 @@
 //   occurrence(s) = number of earlier slots with the same local id
 //   slot_to_row[s] = offsets[l] + occurrence(s)
 // A wavefront takes 64 consecutive slots; the rank of a slot among equal ids
-// of its group comes from a 64-step readlane sweep, and per-wave running
-// counts per expert live in LDS.  A per-expert exclusive prefix over the
+// of its group comes from bit-sliced ballots (one per bit of the local id),
+// and per-wave running counts per expert live in LDS.  A per-expert exclusive prefix over the
 // waves (then over blocks) turns group ranks into occurrences.
 //
 //   N <= 64         : one wavefront does everything (decode batches)
@@ -39,8 +39,8 @@ __device__ __forceinline__ int local_of(int id, const int32_t* __restrict__ emap
   return local_expert(id, emap, Eg, El);
 }
 
-__device__ __forceinline__ void group_rank(int l, int lane, int& below, int& total) {
-  wave_group_rank(l, lane, below, total);
+__device__ __forceinline__ void group_rank(int l, int El, int& below, int& total) {
+  wave_group_rank(l, El, below, total);
 }
 
 // Ranks the 64-slot groups [first_slot + 64*g, ...) of one wave; returns the
@@ -59,7 +59,7 @@ __device__ __forceinline__ void wave_ranks(const int32_t* __restrict__ ids, int6
     const int64_t s = s0 + lane;
     const int l = (s < N) ? local_of(ids[s], emap, Eg, El) : -1;
     int below, total;
-    group_rank(l, lane, below, total);
+    group_rank(l, El, below, total);
     if (l >= 0) rank[g] = run[l] + below;
     // one writer per distinct id: the last occurrence in this group
     if (l >= 0 && below == total - 1) run[l] += total;
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(64) void compact_wave_kernel(
   const int lane = threadIdx.x;
   const int l = lane < N ? local_of(ids[lane], emap, Eg, El) : -1;
   int below, total;
-  group_rank(l, lane, below, total);
+  group_rank(l, El, below, total);
   int carry = 0;
   for (int c0 = 0; c0 < El; c0 += 64) {
     const int e = c0 + lane;

@@ -488,7 +488,7 @@ __global__ __launch_bounds__(kCompactBlockSlots) void topk8_count_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l = id >= 0 ? local_expert(id, emap, Eg, El) : -1;
   int below, total;
-  wave_group_rank(l, lane, below, total);
+  wave_group_rank(l, El, below, total);
   __syncthreads();  // run is zero
   int* runw = run + wave * El;
   if (l >= 0 && below == total - 1) runw[l] = total;  // one writer per distinct id of the wave
