@@ -221,30 +221,61 @@ __global__ __launch_bounds__(kThreads) void compact_count_kernel(
   if (s < N && loc[0] >= 0) s2r[s] = run[wave * El + loc[0]] + rank[0];  // rank inside this block
 }
 
+// Per-expert exclusive prefix over the B count blocks (each block's base row
+// per expert), the expert totals and the offsets, in one block.  Thread t
+// takes expert t % El and part t / El of the count blocks (P = kThreads / El
+// parts of consecutive blocks), so a thread reads few counts and none of its
+// loads waits on another: the part sums, a prefix over the parts per expert,
+// the scan over experts, then each part writes its blocks' bases.
 __global__ __launch_bounds__(kThreads) void compact_scan_kernel(
     int32_t* __restrict__ block_counts, int B, int El, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets) {
   extern __shared__ int lds[];
-  int* cnt = lds;           // [El]
-  int* offs = cnt + El;     // [El + 1]
-  int* tmp = offs + El + 1; // [kWaves + 1]
-  for (int e = threadIdx.x; e < El; e += kThreads) {
+  const int P = kThreads / El;  // El <= kThreads
+  int* cnt = lds;                  // [El]
+  int* offs = cnt + El;            // [El + 1]
+  int* tmp = offs + El + 1;        // [kWaves + 1]
+  int* part = tmp + kWaves + 1;    // [P][El]
+  const int e = (int)threadIdx.x % El, p = (int)threadIdx.x / El;
+  const int per = (B + P - 1) / P;
+  const int b0 = p < P ? min(B, p * per) : B, b1 = min(B, b0 + per);
+  constexpr int kBatch = 8;
+  int sum = 0;
+  for (int b = b0; b < b1; b += kBatch) {
+    int c[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) c[j] = (b + j < b1) ? block_counts[(int64_t)(b + j) * El + e] : 0;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) sum += c[j];
+  }
+  if (p < P) part[p * El + e] = sum;
+  __syncthreads();
+  for (int x = threadIdx.x; x < El; x += kThreads) {
     int acc = 0;
-    for (int b = 0; b < B; ++b) {
-      const int c = block_counts[(int64_t)b * El + e];
-      block_counts[(int64_t)b * El + e] = acc;
+    for (int q = 0; q < P; ++q) {
+      const int c = part[q * El + x];
+      part[q * El + x] = acc;
       acc += c;
     }
-    cnt[e] = acc;
+    cnt[x] = acc;
   }
   __syncthreads();
   scan_counts(cnt, El, offs, tmp);
-  for (int e = threadIdx.x; e < El; e += kThreads) {
-    counts[e] = cnt[e];
-    const int base = offs[e];
-    for (int b = 0; b < B; ++b) block_counts[(int64_t)b * El + e] += base;
+  if (p < P) {
+    int acc = offs[e] + part[p * El + e];
+    for (int b = b0; b < b1; b += kBatch) {
+      int c[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) c[j] = (b + j < b1) ? block_counts[(int64_t)(b + j) * El + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if (b + j < b1) block_counts[(int64_t)(b + j) * El + e] = acc;
+        acc += c[j];
+      }
+    }
   }
-  for (int e = threadIdx.x; e <= El; e += kThreads) offsets[e] = offs[e];
+  for (int x = threadIdx.x; x < El; x += kThreads) counts[x] = cnt[x];
+  for (int x = threadIdx.x; x <= El; x += kThreads) offsets[x] = offs[x];
 }
 
 __global__ __launch_bounds__(256) void compact_scatter_kernel(
@@ -466,7 +497,8 @@ hipError_t launch_compact_scatter_phase(const int32_t* ids, int64_t N, const int
     return hipGetLastError();
   }
   hipLaunchKernelGGL(compact_scan_kernel, dim3(1), dim3(kThreads),
-                     sizeof(int) * ((size_t)El + El + 1 + kWaves + 1), stream, bc, (int)B, El, counts,
+                     sizeof(int) * ((size_t)El + El + 1 + kWaves + 1 + (size_t)(kThreads / El) * El), stream, bc,
+                     (int)B, El, counts,
                      offsets);
   err = hipGetLastError();
   if (err != hipSuccess) return err;

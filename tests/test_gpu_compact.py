@@ -44,6 +44,9 @@ def test_mxfp4_decode_routes(T, routes):
     (512, 8, 128, 128),      # 4096 slots: largest single-block size
     (513, 8, 128, 128),      # 4104 slots: smallest multi-block size
     (65536, 8, 160, 160),    # 524288 slots
+    (9000, 8, 256, 40),      # 71 count blocks, 25 parts of 3 in the scan: empty last parts
+    (10000, 8, 1024, 768),   # 79 count blocks, one part per expert in the scan
+    (70000, 1, 256, 1),      # 69 count blocks, one local expert: 1024 parts of one block
     (333, 3, 256, 40),
     (1000, 6, 256, 1),       # one local expert
     (3000, 8, 1024, 768),    # widest supported local expert set
