@@ -141,3 +141,29 @@ def test_sigmoid_gate_extremes():
     f = np.stack(rows)
     check_gate(f, "f32", K, False, "extremes", "sigmoid")
     check_gate(f, "f32", K, True, "extremes", "sigmoid")
+
+
+@pytest.mark.parametrize("E", [64, 96, 128, 160, 192])
+@pytest.mark.parametrize("off", [1, 4])
+def test_gate_misaligned_logits(E, off):
+    # logits starting 2 or 8 bytes past an aligned address: the fast kernel
+    # needs 16-byte rows for E % 64 == 0 and 8-byte rows otherwise, so these
+    # take its 8-byte-load form or the generic kernel; results must not change
+    T, K = 777, 8
+    logits = synth.gate_logits_bf16(T, E, seed=E + off, tie_fraction=0.05)
+    full = dev_bf16(logits)
+    base = torch.empty(T * E + off, dtype=torch.bfloat16, device=DEV)
+    base[off:].copy_(full.reshape(-1))
+    view = base[off:].view(T, E)
+    assert view.data_ptr() % 16 != 0
+    for renorm in (False, True):
+        w_ref, ids_ref, tei_ref = oracle.topk_softmax(logits, K, renorm, "bf16")
+        print(f"[gate] misaligned by {off} elements E={E} renorm={renorm}", flush=True)
+        w, ids, tei = moe.moe_topk_softmax(view, K, renorm)
+        w_al, ids_al, _ = moe.moe_topk_softmax(full, K, renorm)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_i(ids), ids_ref) and np.array_equal(host_i(tei), tei_ref)
+        assert torch.equal(ids, ids_al)
+        wd = w.cpu().numpy().astype(np.float64)
+        rel = np.max(np.maximum(np.abs(wd - w_ref) - 2.0 ** -126, 0.0) / np.abs(w_ref))
+        assert rel <= W_RTOL, f"weights rel err {rel:.3e}"
