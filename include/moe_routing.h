@@ -44,7 +44,9 @@ typedef enum moe_status {
   MOE_ERR_INVALID_ARG = 1, /* null pointer, negative or inconsistent size */
   MOE_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels implement */
   MOE_ERR_HIP = 3,         /* a HIP launch or device query failed */
-  MOE_ERR_WORKSPACE = 4    /* workspace missing or smaller than required */
+  MOE_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
+  MOE_ERR_SCRATCH_LIMIT = 5 /* the call needs more than the library's fixed
+                               scratch (moe_grouped_ffn_noalloc) */
 } moe_status;
 
 typedef enum moe_dtype {
@@ -213,6 +215,32 @@ int moe_grouped_ffn(const void* x, int x_dtype, int64_t T, int32_t K, int32_t H,
                     void* workspace, size_t workspace_bytes, void* stream);
 size_t moe_grouped_ffn_workspace_bytes(int64_t T, int32_t K, int32_t H, int32_t F, int32_t E_local,
                                        int w_dtype);
+
+/*
+ * moe_grouped_ffn_noalloc -- moe_grouped_ffn for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same computation and the same
+ * results, with the act rows kept in a fixed scratch array of the library
+ * instead of a caller workspace.  No hipMalloc, hipFree or allocating call is
+ * made.
+ *
+ * Arguments as for moe_grouped_ffn, without workspace and workspace_bytes.
+ * Scratch: 64 MiB per GPU (a device array of the library, held by each GPU
+ * it runs on until the process ends); the call needs
+ * moe_grouped_ffn_workspace_bytes(...) of it -- T*K*F*2 bytes for bf16,
+ * MXFP4 and tile-packed weights, T*K*F*4 for f32 -- and returns
+ * MOE_ERR_SCRATCH_LIMIT, before anything is enqueued, when that exceeds
+ * 64 MiB.  The scratch of the current device is used (the stream must belong
+ * to it).  Every call on one GPU shares that GPU's scratch: calls that may
+ * overlap on one GPU (different streams without ordering) race and must not
+ * be issued.  Nothing in the scratch needs clearing between calls (every act
+ * row is written before it is read).
+ */
+int moe_grouped_ffn_noalloc(const void* x, int x_dtype, int64_t T, int32_t K, int32_t H, int32_t F,
+                            int32_t E_local, const void* w1, const uint8_t* w1_scale, const void* w2,
+                            const uint8_t* w2_scale, int w_dtype, const int32_t* counts,
+                            const int32_t* offsets, const int32_t* row_to_slot, void* y, int y_dtype,
+                            void* stream);
 
 /*
  * moe_grouped_ffn_control -- the same FFN as moe_grouped_ffn, run by the

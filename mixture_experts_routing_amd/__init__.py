@@ -19,7 +19,7 @@ _LIB = _lib.load()
 
 __all__ = [
     "moe_topk_softmax", "moe_topk_sigmoid", "moe_route_compact", "moe_route_align", "moe_grouped_ffn",
-    "moe_grouped_ffn_control", "moe_fused_experts", "moe_topk_compact", "moe_combine", "moe_pack_ffn_weights", "moe_layer",
+    "moe_grouped_ffn_noalloc", "moe_grouped_ffn_control", "moe_fused_experts", "moe_topk_compact", "moe_combine", "moe_pack_ffn_weights", "moe_layer",
     "MOE_F32", "MOE_BF16", "MOE_MXFP4", "MOE_BF16_TILED", "MoeError", "library_path",
 ]
 
@@ -254,6 +254,34 @@ def moe_grouped_ffn(x: torch.Tensor, K: int, w1: torch.Tensor, w2: torch.Tensor,
                                 _ptr(w2_scale), w_dt, _ptr(counts), _ptr(offsets), _ptr(row_to_slot), _ptr(y),
                                 _dt(y), _ptr(workspace), workspace.numel(), _stream(stream, dev)),
            "moe_grouped_ffn")
+    return y
+
+
+def moe_grouped_ffn_noalloc(x: torch.Tensor, K: int, w1: torch.Tensor, w2: torch.Tensor, counts: torch.Tensor,
+                            offsets: torch.Tensor, row_to_slot: torch.Tensor, w1_scale: Optional[torch.Tensor] = None,
+                            w2_scale: Optional[torch.Tensor] = None, y_dtype: Optional[torch.dtype] = None,
+                            y: Optional[torch.Tensor] = None, stream=None, tiled: bool = False):
+    """moe_grouped_ffn with the act rows in the library's fixed per-GPU scratch
+    (64 MiB) instead of a workspace: the library allocates nothing.  Same
+    arguments (no workspace) and result; raises MoeError
+    (MOE_ERR_SCRATCH_LIMIT) when the act rows exceed the scratch.  y must be
+    given by callers that cannot allocate."""
+    dev = _dev(x, w1, w2, counts, offsets, row_to_slot, w1_scale, w2_scale, y)
+    T, H = x.shape
+    E_local = w1.shape[0]
+    if w1.dtype == torch.uint8:
+        w_dt, F = MOE_MXFP4, w2.shape[2] * 2
+    else:
+        w_dt, F = _dt(w1), w2.shape[2]
+    if tiled:
+        if w_dt != MOE_BF16:
+            raise MoeError("tiled weights must be bfloat16")
+        w_dt = MOE_BF16_TILED
+    if y is None:
+        y = torch.empty((T * K, H), dtype=y_dtype or x.dtype, device=dev)
+    _check(_LIB.moe_grouped_ffn_noalloc(_ptr(x), _dt(x), T, K, H, F, E_local, _ptr(w1), _ptr(w1_scale), _ptr(w2),
+                                        _ptr(w2_scale), w_dt, _ptr(counts), _ptr(offsets), _ptr(row_to_slot),
+                                        _ptr(y), _dt(y), _stream(stream, dev)), "moe_grouped_ffn_noalloc")
     return y
 
 

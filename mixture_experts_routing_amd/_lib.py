@@ -10,7 +10,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libmoe_routing.so")
 HEADER = os.path.join(os.path.dirname(PKG_DIR), "include", "moe_routing.h")
 
-MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP, MOE_ERR_WORKSPACE = range(5)
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP, MOE_ERR_WORKSPACE, MOE_ERR_SCRATCH_LIMIT = range(6)
 MOE_F32, MOE_BF16, MOE_MXFP4, MOE_BF16_TILED = range(4)
 
 _p = ctypes.c_void_p
@@ -31,6 +31,8 @@ SIGNATURES = {
     "moe_grouped_ffn": (_int, [_p, _int, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _int, _p, _p, _p, _p, _int,
                                _p, _sz, _p]),
     "moe_grouped_ffn_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32, _int]),
+    "moe_grouped_ffn_noalloc": (_int, [_p, _int, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _int, _p, _p, _p, _p,
+                                       _int, _p]),
     "moe_grouped_ffn_control": (_int, [_p, _int, _i64, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _int, _p, _p, _p, _p,
                                        _int, _p, _sz, _p]),
     "moe_grouped_ffn_control_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32, _int]),

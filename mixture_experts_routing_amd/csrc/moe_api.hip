@@ -1,6 +1,8 @@
 // C ABI entry points: host-side argument checks, then the launchers.
 // Every check runs before anything is enqueued, so an error leaves the
 // outputs untouched and the stream unchanged.
+#include <mutex>
+
 #include "moe_internal.h"
 
 namespace {
@@ -28,6 +30,7 @@ const char* moe_status_string(int s) {
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
     case MOE_ERR_HIP: return "MOE_ERR_HIP";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_SCRATCH_LIMIT: return "MOE_ERR_SCRATCH_LIMIT";
     default: return "MOE_ERR_UNKNOWN";
   }
 }
@@ -136,10 +139,13 @@ size_t moe_grouped_ffn_workspace_bytes(int64_t T, int32_t K, int32_t H, int32_t 
   return moe::grouped_ffn_workspace_bytes(T * K, H, F, E_local, w_dtype);
 }
 
-int moe_grouped_ffn(const void* x, int x_dtype, int64_t T, int32_t K, int32_t H, int32_t F, int32_t E_local,
-                    const void* w1, const uint8_t* w1_scale, const void* w2, const uint8_t* w2_scale, int w_dtype,
-                    const int32_t* counts, const int32_t* offsets, const int32_t* row_to_slot, void* y, int y_dtype,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+// Checks shared by moe_grouped_ffn and moe_grouped_ffn_noalloc (everything but
+// the workspace).  Returns MOE_OK, an error, or -1 for the valid no-op T == 0.
+int check_grouped_ffn(const void* x, int x_dtype, int64_t T, int32_t K, int32_t H, int32_t F, int32_t E_local,
+                      const void* w1, const uint8_t* w1_scale, const void* w2, const uint8_t* w2_scale, int w_dtype,
+                      const int32_t* counts, const int32_t* offsets, const int32_t* row_to_slot, const void* y,
+                      int y_dtype) {
   if (T < 0 || K < 1 || H < 1 || F < 1 || E_local < 1) return MOE_ERR_INVALID_ARG;
   if (y_dtype != MOE_F32 && y_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   const bool f32_pair = (x_dtype == MOE_F32 && w_dtype == MOE_F32);
@@ -151,19 +157,76 @@ int moe_grouped_ffn(const void* x, int x_dtype, int64_t T, int32_t K, int32_t H,
   if (!f32_pair && (H % 32 != 0 || F % 32 != 0)) return MOE_ERR_UNSUPPORTED;
   if (T * (int64_t)K >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
   if (f32_pair && T * (int64_t)K * (int64_t)(H > F ? H : F) >= ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
-  if (T == 0) return MOE_OK;
+  if (T == 0) return -1;
   if (!x || !w1 || !w2 || !counts || !offsets || !row_to_slot || !y) return MOE_ERR_INVALID_ARG;
   if (mx_pair && (!w1_scale || !w2_scale)) return MOE_ERR_INVALID_ARG;
   if (!f32_pair) {
     // bf16 rows are read as 16-byte vectors
     if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16)) return MOE_ERR_INVALID_ARG;
+    if (!aligned(y, 16)) return MOE_ERR_INVALID_ARG;  // rows are stored as 16-byte pieces
   }
+  return MOE_OK;
+}
+
+// Scratch of moe_grouped_ffn_noalloc: the act rows that moe_grouped_ffn keeps
+// in the caller's workspace.  Each GPU holds its own copy of the array from
+// the time the library's code is loaded on it until the process ends.  The
+// array's name is a host-side handle, not a device address: the address is
+// looked up once per device (hipGetSymbolAddress, with that device current)
+// and only that address is passed to the kernels.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (!p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+int moe_grouped_ffn(const void* x, int x_dtype, int64_t T, int32_t K, int32_t H, int32_t F, int32_t E_local,
+                    const void* w1, const uint8_t* w1_scale, const void* w2, const uint8_t* w2_scale, int w_dtype,
+                    const int32_t* counts, const int32_t* offsets, const int32_t* row_to_slot, void* y, int y_dtype,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_grouped_ffn(x, x_dtype, T, K, H, F, E_local, w1, w1_scale, w2, w2_scale, w_dtype, counts,
+                                   offsets, row_to_slot, y, y_dtype);
+  if (st != MOE_OK) return st < 0 ? MOE_OK : st;
   const size_t need = moe::grouped_ffn_workspace_bytes(T * K, H, F, E_local, w_dtype);
   if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return MOE_ERR_INVALID_ARG;
-  if (!f32_pair && !aligned(y, 16)) return MOE_ERR_INVALID_ARG;  // rows are stored as 16-byte pieces
   return hip_status(moe::launch_grouped_ffn(x, x_dtype, T, K, H, F, E_local, w1, w1_scale, w2, w2_scale, w_dtype,
                                             counts, offsets, row_to_slot, y, y_dtype, workspace,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int moe_grouped_ffn_noalloc(const void* x, int x_dtype, int64_t T, int32_t K, int32_t H, int32_t F, int32_t E_local,
+                            const void* w1, const uint8_t* w1_scale, const void* w2, const uint8_t* w2_scale,
+                            int w_dtype, const int32_t* counts, const int32_t* offsets, const int32_t* row_to_slot,
+                            void* y, int y_dtype, void* stream) {
+  const int st = check_grouped_ffn(x, x_dtype, T, K, H, F, E_local, w1, w1_scale, w2, w2_scale, w_dtype, counts,
+                                   offsets, row_to_slot, y, y_dtype);
+  if (st != MOE_OK) return st < 0 ? MOE_OK : st;
+  // the act rows must fit the scratch array; checked before any HIP call
+  if (moe::grouped_ffn_workspace_bytes(T * K, H, F, E_local, w_dtype) > kScratchBytes) return MOE_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  const int sst = scratch_of_current_device(&ws);
+  if (sst != MOE_OK) return sst;
+  return hip_status(moe::launch_grouped_ffn(x, x_dtype, T, K, H, F, E_local, w1, w1_scale, w2, w2_scale, w_dtype,
+                                            counts, offsets, row_to_slot, y, y_dtype, ws,
                                             static_cast<hipStream_t>(stream)));
 }
 

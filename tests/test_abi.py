@@ -25,6 +25,7 @@ def test_status_strings(lib):
     assert _lib.status_string(0) == "MOE_OK"
     assert _lib.status_string(1) == "MOE_ERR_INVALID_ARG"
     assert _lib.status_string(4) == "MOE_ERR_WORKSPACE"
+    assert _lib.status_string(5) == "MOE_ERR_SCRATCH_LIMIT"
     assert lib.moe_version().decode().startswith("moe_routing")
 
 
@@ -82,6 +83,29 @@ def test_grouped_ffn_validation(lib):
     assert f(*args(1, 1, 4096, 2048, wsb=need - 1)) == 4
     mis = ctypes.c_void_p(0x1002)  # bf16 operands must be 16-byte aligned
     a = list(args(1, 1, 4096, 2048))
+    a[0] = mis
+    assert f(*a) == 1
+
+
+@_no_gpu
+def test_grouped_ffn_noalloc_validation(lib):
+    # same checks as moe_grouped_ffn (no workspace), plus the fixed 64 MiB
+    # scratch: a call whose act rows exceed it is refused before any HIP call
+    f = lib.moe_grouped_ffn_noalloc
+    def args(T, xdt, wdt, H, F, ydt=1, sc=NULL, E=40):
+        return (FAKE, xdt, T, 6, H, F, E, FAKE, sc, FAKE, sc, wdt, FAKE, FAKE, FAKE, FAKE, ydt, NULL)
+
+    assert f(*args(0, 1, 1, 4096, 2048)) == 0          # T == 0: no-op
+    assert f(*args(2, 0, 1, 4096, 2048)) == 2          # f32 x with bf16 weights
+    assert f(*args(2, 1, 2, 4096, 2048)) == 1          # MXFP4 codes without scales
+    limit = 64 << 20
+    T_fit = limit // (6 * 2048 * 2)                     # act rows exactly fill the scratch
+    assert lib.moe_grouped_ffn_workspace_bytes(T_fit, 6, 4096, 2048, 40, 1) <= limit
+    assert lib.moe_grouped_ffn_workspace_bytes(T_fit + 1, 6, 4096, 2048, 40, 1) > limit
+    assert f(*args(T_fit + 1, 1, 1, 4096, 2048)) == 5   # MOE_ERR_SCRATCH_LIMIT
+    assert f(*args(12288, 1, 3, 2048, 768, E=128)) == 5  # three prefill batches of act rows
+    mis = ctypes.c_void_p(0x1002)
+    a = list(args(2, 1, 1, 4096, 2048))
     a[0] = mis
     assert f(*a) == 1
 
