@@ -54,7 +54,10 @@ typedef enum moe_dtype {
   MOE_BF16 = 1,  /* bfloat16, round-to-nearest-even on every store */
   MOE_MXFP4 = 2, /* OCP MX FP4 (E2M1) codes, 2 per byte, element 2i in the low
                     nibble, plus one E8M0 scale byte (2^(e-127)) per 32
-                    consecutive elements of the reduction dimension */
+                    consecutive elements of the reduction dimension.
+                    Device-side precondition: no scale byte is 0xFF (NaN in
+                    the OCP format); the kernels would read it as an infinite
+                    scale */
   MOE_BF16_TILED = 3 /* expert weights in bfloat16, stored in the tile-packed
                         layout written by moe_pack_ffn_weights */
 } moe_dtype;

@@ -67,6 +67,67 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
 
 
+_I32, _F32, _BF16, _U8 = torch.int32, torch.float32, torch.bfloat16, torch.uint8
+
+
+def _req(t: Optional[torch.Tensor], name: str, dtypes=None, min_numel: Optional[int] = None, shape=None,
+         ndim: Optional[int] = None):
+    """Checks what the C call will read or write through t -- dtype, rank,
+    shape, size -- and raises MoeError before anything reaches the library
+    (the C side sees only pointers: a wrong dtype or a short buffer would be
+    read or written out of bounds on the device)."""
+    if t is None:
+        return
+    if dtypes is not None:
+        dts = dtypes if isinstance(dtypes, tuple) else (dtypes,)
+        if t.dtype not in dts:
+            raise MoeError(f"{name}: dtype {t.dtype}, expected {' or '.join(str(d) for d in dts)}")
+    if ndim is not None and t.dim() != ndim:
+        raise MoeError(f"{name}: {t.dim()}-d tensor, expected {ndim}-d")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise MoeError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise MoeError(f"{name}: {t.numel()} elements, the call needs {min_numel}")
+
+
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _ffn_weights(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, w1_scale, w2_scale):
+    """(T, H, E_local, F, w_dtype) of a grouped-FFN call, after checking that
+    x [T, H], w1 [E, 2F, H] and w2 [E, H, F] agree (MXFP4: uint8 codes
+    [E, 2F, H/2], [E, H, F/2] with scales [E, 2F, H/32], [E, H, F/32])."""
+    _req(x, "x", (_F32, _BF16), ndim=2)
+    _req(w1, "w1", ndim=3)
+    _req(w2, "w2", ndim=3)
+    T, H = x.shape
+    E_local = w1.shape[0]
+    if w1.dtype == _U8:
+        _req(w2, "w2", _U8)
+        F = w2.shape[2] * 2
+        _req(w1, "w1", shape=(E_local, 2 * F, H // 2))
+        _req(w2, "w2", shape=(E_local, H, F // 2))
+        if w1_scale is None or w2_scale is None:
+            raise MoeError("MXFP4 weights need w1_scale and w2_scale")
+        _req(w1_scale, "w1_scale", _U8, shape=(E_local, 2 * F, H // 32))
+        _req(w2_scale, "w2_scale", _U8, shape=(E_local, H, F // 32))
+        return T, H, E_local, F, MOE_MXFP4
+    _req(w1, "w1", (_F32, _BF16))
+    _req(w2, "w2", w1.dtype)
+    F = w2.shape[2]
+    _req(w1, "w1", shape=(E_local, 2 * F, H))
+    _req(w2, "w2", shape=(E_local, H, F))
+    return T, H, E_local, F, _dt(w1)
+
+
+def _route_arrays(T: int, K: int, E_local: int, counts, offsets, s2r=None, r2s=None):
+    _req(counts, "counts", _I32, E_local)
+    _req(offsets, "offsets", _I32, E_local + 1)
+    _req(s2r, "slot_to_row", _I32, T * K)
+    _req(r2s, "row_to_slot", _I32, T * K)
+
+
 def _stream(stream, device) -> int:
     if stream is None:
         stream = torch.cuda.current_stream(device)
@@ -74,8 +135,12 @@ def _stream(stream, device) -> int:
 
 
 def _gate(fn_name, logits, K, renormalize, topk_weights, topk_ids, token_expert_indices, with_indices, stream):
-    dev = _dev(logits)
+    _req(logits, "logits", (_F32, _BF16), ndim=2)
     T, E = logits.shape
+    _req(topk_weights, "topk_weights", _F32, T * K)
+    _req(topk_ids, "topk_ids", _I32, T * K)
+    _req(token_expert_indices, "token_expert_indices", _I32, T * K)
+    dev = _dev(logits)
     if topk_weights is None:
         topk_weights = torch.empty((T, K), dtype=torch.float32, device=dev)
     if topk_ids is None:
@@ -116,10 +181,14 @@ def moe_route_compact(topk_ids: torch.Tensor, expert_map: Optional[torch.Tensor]
                       stream=None):
     """topk_ids [T, K] int32 (global ids), expert_map [E_global] int32 or None
     -> (counts [E_local], offsets [E_local+1], slot_to_row [T*K], row_to_slot [T*K]), all int32."""
-    dev = _dev(topk_ids, expert_map)
+    _req(topk_ids, "topk_ids", _I32, ndim=2)
     T, K = topk_ids.shape
     if E_global is None:
         E_global = expert_map.numel() if expert_map is not None else E_local
+    _req(expert_map, "expert_map", _I32, E_global)
+    if out is not None:
+        _route_arrays(T, K, E_local, *out)
+    dev = _dev(topk_ids, expert_map)
     if out is None:
         counts = torch.empty(E_local, dtype=torch.int32, device=dev)
         offsets = torch.empty(E_local + 1, dtype=torch.int32, device=dev)
@@ -130,7 +199,7 @@ def moe_route_compact(topk_ids: torch.Tensor, expert_map: Optional[torch.Tensor]
     need = route_compact_workspace_bytes(T, K, E_local)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = _nbytes(workspace)
     _check(_LIB.moe_route_compact(_ptr(topk_ids), T, K, _ptr(expert_map), E_global, E_local, _ptr(counts),
                                   _ptr(offsets), _ptr(s2r), _ptr(r2s), _ptr(workspace), ws_bytes,
                                   _stream(stream, dev)), "moe_route_compact")
@@ -145,10 +214,18 @@ def moe_topk_compact(logits: torch.Tensor, K: int, renormalize: bool = False, sc
     inside the gate kernel where the shape allows).  logits [T, E]; scoring
     "softmax" or "sigmoid".  Returns ((topk_weights, topk_ids,
     token_expert_indices or None), (counts, offsets, slot_to_row, row_to_slot))."""
-    dev = _dev(logits, expert_map)
+    _req(logits, "logits", (_F32, _BF16), ndim=2)
     T, E = logits.shape
     if E_local is None:
         E_local = E
+    _req(expert_map, "expert_map", _I32, E)
+    if gate_out is not None:
+        _req(gate_out[0], "topk_weights", _F32, T * K)
+        _req(gate_out[1], "topk_ids", _I32, T * K)
+        _req(gate_out[2], "token_expert_indices", _I32, T * K)
+    if route_out is not None:
+        _route_arrays(T, K, E_local, *route_out)
+    dev = _dev(logits, expert_map)
     if scoring not in ("softmax", "sigmoid"):
         raise MoeError(f"unknown scoring {scoring!r}")
     if gate_out is None:
@@ -165,7 +242,7 @@ def moe_topk_compact(logits: torch.Tensor, K: int, renormalize: bool = False, sc
     need = route_compact_workspace_bytes(T, K, E_local)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = _nbytes(workspace)
     _check(_LIB.moe_topk_compact(_ptr(logits), _dt(logits), T, E, K, int(renormalize),
                                  0 if scoring == "softmax" else 1, _ptr(tw), _ptr(tid), _ptr(tei), _ptr(expert_map),
                                  E_local, _ptr(counts), _ptr(offsets), _ptr(s2r), _ptr(r2s), _ptr(workspace),
@@ -181,13 +258,20 @@ def moe_route_align(topk_ids: torch.Tensor, expert_map: Optional[torch.Tensor], 
                     E_global: Optional[int] = None, out=None, workspace: Optional[torch.Tensor] = None, stream=None):
     """Block-aligned layout: -> (padded_offsets [E_local+1], sorted_slots [cap_rows],
     block_expert [cap_blocks], slot_to_row [T*K]), all int32 (see moe_route_align)."""
-    dev = _dev(topk_ids, expert_map)
+    _req(topk_ids, "topk_ids", _I32, ndim=2)
     T, K = topk_ids.shape
     N = T * K
     if E_global is None:
         E_global = expert_map.numel() if expert_map is not None else E_local
+    _req(expert_map, "expert_map", _I32, E_global)
     cap_rows = N + E_local * (block_size - 1)
     cap_blocks = -(-N // block_size) + E_local
+    if out is not None:
+        _req(out[0], "padded_offsets", _I32, E_local + 1)
+        _req(out[1], "sorted_slots", _I32, cap_rows)
+        _req(out[2], "block_expert", _I32, cap_blocks)
+        _req(out[3], "slot_to_row", _I32, N)
+    dev = _dev(topk_ids, expert_map)
     if out is None:
         out = (torch.empty(E_local + 1, dtype=torch.int32, device=dev),
                torch.empty(cap_rows, dtype=torch.int32, device=dev),
@@ -199,7 +283,7 @@ def moe_route_align(topk_ids: torch.Tensor, expert_map: Optional[torch.Tensor], 
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     _check(_LIB.moe_route_align(_ptr(topk_ids), T, K, _ptr(expert_map), E_global, E_local, block_size, _ptr(poff),
                                 _ptr(sorted_slots), _ptr(block_expert), _ptr(s2r), _ptr(workspace),
-                                workspace.numel(), _stream(stream, dev)), "moe_route_align")
+                                _nbytes(workspace), _stream(stream, dev)), "moe_route_align")
     return poff, sorted_slots, block_expert, s2r
 
 
@@ -212,8 +296,12 @@ def moe_pack_ffn_weights(w1: torch.Tensor, w2: torch.Tensor, w1_tiled: Optional[
     """bf16 w1 [E_local, 2F, H], w2 [E_local, H, F] -> the same weights in the
     tile-packed layout (tensors of the same shapes and dtype, whose memory
     order is the packed one); pass them to moe_grouped_ffn with tiled=True."""
-    dev = _dev(w1, w2)
+    _req(w2, "w2", _BF16, ndim=3)
     E_local, H, F = w2.shape
+    _req(w1, "w1", _BF16, shape=(E_local, 2 * F, H))
+    _req(w1_tiled, "w1_tiled", _BF16, shape=(E_local, 2 * F, H))
+    _req(w2_tiled, "w2_tiled", _BF16, shape=(E_local, H, F))
+    dev = _dev(w1, w2, w1_tiled, w2_tiled)
     if w1_tiled is None:
         w1_tiled = torch.empty_like(w1)
     if w2_tiled is None:
@@ -232,15 +320,10 @@ def moe_grouped_ffn(x: torch.Tensor, K: int, w1: torch.Tensor, w2: torch.Tensor,
     uint8 MXFP4 codes [E_local, 2F, H/2], [E_local, H, F/2] with e8m0 scales,
     or (tiled=True) bf16 weights from moe_pack_ffn_weights.
     Returns y [T*K, H] in the expert-grouped row order (rows >= R unwritten)."""
-    dev = _dev(x, w1, w2, counts, offsets, row_to_slot, w1_scale, w2_scale)
-    T, H = x.shape
-    E_local = w1.shape[0]
-    if w1.dtype == torch.uint8:
-        w_dt = MOE_MXFP4
-        F = w2.shape[2] * 2
-    else:
-        w_dt = _dt(w1)
-        F = w2.shape[2]
+    T, H, E_local, F, w_dt = _ffn_weights(x, w1, w2, w1_scale, w2_scale)
+    _route_arrays(T, K, E_local, counts, offsets, None, row_to_slot)
+    _req(y, "y", (_F32, _BF16), T * K * H)
+    dev = _dev(x, w1, w2, counts, offsets, row_to_slot, w1_scale, w2_scale, y)
     if tiled:
         if w_dt != MOE_BF16:
             raise MoeError("tiled weights must be bfloat16")
@@ -252,7 +335,7 @@ def moe_grouped_ffn(x: torch.Tensor, K: int, w1: torch.Tensor, w2: torch.Tensor,
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     _check(_LIB.moe_grouped_ffn(_ptr(x), _dt(x), T, K, H, F, E_local, _ptr(w1), _ptr(w1_scale), _ptr(w2),
                                 _ptr(w2_scale), w_dt, _ptr(counts), _ptr(offsets), _ptr(row_to_slot), _ptr(y),
-                                _dt(y), _ptr(workspace), workspace.numel(), _stream(stream, dev)),
+                                _dt(y), _ptr(workspace), _nbytes(workspace), _stream(stream, dev)),
            "moe_grouped_ffn")
     return y
 
@@ -266,13 +349,10 @@ def moe_grouped_ffn_noalloc(x: torch.Tensor, K: int, w1: torch.Tensor, w2: torch
     arguments (no workspace) and result; raises MoeError
     (MOE_ERR_SCRATCH_LIMIT) when the act rows exceed the scratch.  y must be
     given by callers that cannot allocate."""
+    T, H, E_local, F, w_dt = _ffn_weights(x, w1, w2, w1_scale, w2_scale)
+    _route_arrays(T, K, E_local, counts, offsets, None, row_to_slot)
+    _req(y, "y", (_F32, _BF16), T * K * H)
     dev = _dev(x, w1, w2, counts, offsets, row_to_slot, w1_scale, w2_scale, y)
-    T, H = x.shape
-    E_local = w1.shape[0]
-    if w1.dtype == torch.uint8:
-        w_dt, F = MOE_MXFP4, w2.shape[2] * 2
-    else:
-        w_dt, F = _dt(w1), w2.shape[2]
     if tiled:
         if w_dt != MOE_BF16:
             raise MoeError("tiled weights must be bfloat16")
@@ -295,13 +375,10 @@ def moe_grouped_ffn_control(x: torch.Tensor, K: int, w1: torch.Tensor, w2: torch
                             workspace: Optional[torch.Tensor] = None, stream=None):
     """moe_grouped_ffn run by the generic atomic-counter scheduler (the A/B
     control); same arguments and result layout."""
-    dev = _dev(x, w1, w2, counts, offsets, row_to_slot, w1_scale, w2_scale)
-    T, H = x.shape
-    E_local = w1.shape[0]
-    if w1.dtype == torch.uint8:
-        w_dt, F = MOE_MXFP4, w2.shape[2] * 2
-    else:
-        w_dt, F = _dt(w1), w2.shape[2]
+    T, H, E_local, F, w_dt = _ffn_weights(x, w1, w2, w1_scale, w2_scale)
+    _route_arrays(T, K, E_local, counts, offsets, None, row_to_slot)
+    _req(y, "y", (_F32, _BF16), T * K * H)
+    dev = _dev(x, w1, w2, counts, offsets, row_to_slot, w1_scale, w2_scale, y)
     if y is None:
         y = torch.empty((T * K, H), dtype=y_dtype or x.dtype, device=dev)
     need = grouped_ffn_control_workspace_bytes(T, K, H, F, E_local, w_dt)
@@ -309,7 +386,7 @@ def moe_grouped_ffn_control(x: torch.Tensor, K: int, w1: torch.Tensor, w2: torch
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     _check(_LIB.moe_grouped_ffn_control(_ptr(x), _dt(x), T, K, H, F, E_local, _ptr(w1), _ptr(w1_scale), _ptr(w2),
                                         _ptr(w2_scale), w_dt, _ptr(counts), _ptr(offsets), _ptr(row_to_slot),
-                                        _ptr(y), _dt(y), _ptr(workspace), workspace.numel(), _stream(stream, dev)),
+                                        _ptr(y), _dt(y), _ptr(workspace), _nbytes(workspace), _stream(stream, dev)),
            "moe_grouped_ffn_control")
     return y
 
@@ -317,9 +394,13 @@ def moe_grouped_ffn_control(x: torch.Tensor, K: int, w1: torch.Tensor, w2: torch
 def moe_combine(y: torch.Tensor, topk_weights: torch.Tensor, slot_to_row: torch.Tensor,
                 out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None, stream=None):
     """y [R', H] grouped rows, topk_weights [T, K] f32, slot_to_row [T*K] -> out [T, H]."""
-    dev = _dev(y, topk_weights, slot_to_row)
+    _req(y, "y", (_F32, _BF16), ndim=2)
+    _req(topk_weights, "topk_weights", _F32, ndim=2)
     T, K = topk_weights.shape
     H = y.shape[1]
+    _req(slot_to_row, "slot_to_row", _I32, T * K)
+    _req(out, "out", (_F32, _BF16), T * H)
+    dev = _dev(y, topk_weights, slot_to_row, out)
     if out is None:
         out = torch.empty((T, H), dtype=out_dtype or y.dtype, device=dev)
     _check(_LIB.moe_combine(_ptr(y), _dt(y), _ptr(topk_weights), _ptr(slot_to_row), T, K, H, _ptr(out), _dt(out),
@@ -340,16 +421,18 @@ def moe_fused_experts(x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: tor
     combine in two launches.  x [T, H] bf16, topk_ids / topk_weights [T, K],
     weights as for moe_grouped_ffn (bf16 or MXFP4).
     Returns (out [T, H], (counts, offsets, slot_to_row, row_to_slot))."""
-    dev = _dev(x, topk_ids, topk_weights, w1, w2, expert_map, w1_scale, w2_scale)
-    T, H = x.shape
+    T, H, E_local, F, w_dt = _ffn_weights(x, w1, w2, w1_scale, w2_scale)
+    _req(topk_ids, "topk_ids", _I32, ndim=2)
     K = topk_ids.shape[1]
-    E_local = w1.shape[0]
+    _req(topk_ids, "topk_ids", shape=(T, K))
+    _req(topk_weights, "topk_weights", _F32, shape=(T, K))
     if E_global is None:
         E_global = expert_map.numel() if expert_map is not None else E_local
-    if w1.dtype == torch.uint8:
-        w_dt, F = MOE_MXFP4, w2.shape[2] * 2
-    else:
-        w_dt, F = _dt(w1), w2.shape[2]
+    _req(expert_map, "expert_map", _I32, E_global)
+    if routes is not None:
+        _route_arrays(T, K, E_local, *routes)
+    _req(out, "out", (_F32, _BF16), T * H)
+    dev = _dev(x, topk_ids, topk_weights, w1, w2, expert_map, w1_scale, w2_scale, out)
     if out is None:
         out = torch.empty((T, H), dtype=out_dtype or x.dtype, device=dev)
     if routes is None:
@@ -364,7 +447,7 @@ def moe_fused_experts(x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: tor
     _check(_LIB.moe_fused_experts(_ptr(x), _dt(x), T, K, H, F, _ptr(topk_ids), _ptr(topk_weights),
                                   _ptr(expert_map), E_global, E_local, _ptr(w1), _ptr(w1_scale), _ptr(w2),
                                   _ptr(w2_scale), w_dt, _ptr(counts), _ptr(offsets), _ptr(s2r), _ptr(r2s),
-                                  _ptr(out), _dt(out), _ptr(workspace), workspace.numel(), _stream(stream, dev)),
+                                  _ptr(out), _dt(out), _ptr(workspace), _nbytes(workspace), _stream(stream, dev)),
            "moe_fused_experts")
     return out, routes
 

@@ -260,27 +260,32 @@ def decode_case(pattern: str, map_kind: str = "contiguous", seed: int = 0, weigh
 # config 3: gate throughput
 
 
-def gate_logits_bf16(T: int, E: int, seed: int, tie_fraction: float = 0.01) -> np.ndarray:
+def gate_logits_bf16(T: int, E: int, seed: int, tie_fraction: float = 0.01, K: int = 8) -> np.ndarray:
     """bf16 logits 2*N(0,1) [T, E] with exact ties injected into ~1% of rows.
 
-    Half of the chosen rows copy the row's largest value onto another random
-    expert; the other half copy a random expert's value onto another random
-    expert.  Ties between distinct bf16 draws also occur naturally (bf16 has an
-    8-bit significand)."""
+    Half of the chosen rows get a boundary tie: the value ranked K-th in the
+    row (order: value descending, index ascending) is copied onto a random
+    expert ranked below K, so the K-th place is decided by the lower-index
+    rule.  The other half copy the row's largest value onto another random
+    expert.  (With E <= K every chosen row gets the second kind.)  Ties
+    between distinct bf16 draws also occur naturally (bf16 has an 8-bit
+    significand)."""
     bits = bf16_normal((T, E), 2.0, seed, _LOGITS)
     n_ties = int(round(T * tie_fraction))
     if n_ties and E > 1:
         r = _rng(seed, _TIES)
         rows = r.choice(T, size=n_ties, replace=False)
         for i, t in enumerate(rows):
-            if i % 2 == 0:
-                # bf16 bit patterns are sign-magnitude; decode to float32 to find the max
-                f = (bits[t].astype(np.uint32) << np.uint32(16)).view(np.float32)
-                src = int(np.argmax(f))
+            # bf16 bit patterns are sign-magnitude; decode to float32 to rank
+            f = (bits[t].astype(np.uint32) << np.uint32(16)).view(np.float32)
+            if i % 2 == 0 and E > K:
+                order = np.lexsort((np.arange(E), -f.astype(np.float64)))
+                src = int(order[K - 1])
+                dst = int(order[K + int(r.integers(E - K))])
             else:
-                src = int(r.integers(E))
-            dst = int(r.integers(E - 1))
-            dst = dst + 1 if dst >= src else dst
+                src = int(np.argmax(f))
+                dst = int(r.integers(E - 1))
+                dst = dst + 1 if dst >= src else dst
             bits[t, dst] = bits[t, src]
     return bits
 
@@ -291,7 +296,7 @@ def gate_case(E: int, T: int = 65536, K: int = 8, seed: int = 0, renormalize: bo
         name=f"gate_T{T}_E{E}_K{K}", T=T, E_global=E, E_local=E, K=K, H=0, F=0,
         renormalize=renormalize, x_dtype="bf16", w_dtype="bf16", out_dtype="bf16",
         x=np.zeros((T, 0), np.uint16), w1=None, w2=None,
-        logits=gate_logits_bf16(T, E, seed), logits_dtype="bf16",
+        logits=gate_logits_bf16(T, E, seed, K=K), logits_dtype="bf16",
     )
 
 

@@ -161,3 +161,46 @@ def test_topk_compact_validation(lib):
     assert f(*args(ws=NULL)) == 4               # 32768 slots need the count table
     need = lib.moe_route_compact_workspace_bytes(4096, 8, 128)
     assert f(*args(wsb=need - 1)) == 4
+
+
+def test_binding_checks_dtypes_shapes_and_sizes():
+    # The binding refuses tensors whose dtype, shape or size differs from what
+    # the C call reads or writes, before any pointer reaches the library (CPU
+    # tensors: the checks run before the device check).
+    import mixture_experts_routing_amd as moe
+
+    i32, i64, f32, bf16, u8 = torch.int32, torch.int64, torch.float32, torch.bfloat16, torch.uint8
+    z = lambda shape, dt: torch.zeros(shape, dtype=dt)
+    with pytest.raises(moe.MoeError, match="dtype"):
+        moe.moe_topk_softmax(z((4, 8), i64), 2)                       # integer logits
+    with pytest.raises(moe.MoeError, match="elements"):
+        moe.moe_topk_softmax(z((4, 8), bf16), 2, topk_ids=z(7, i32))  # ids buffer too short
+    with pytest.raises(moe.MoeError, match="dtype"):
+        moe.moe_route_compact(z((2, 6), i64), None, 8)                # int64 ids (torch.topk's)
+    with pytest.raises(moe.MoeError, match="elements"):
+        moe.moe_route_compact(z((2, 6), i32), z(100, i32), 40, E_global=256)  # map shorter than E_global
+    with pytest.raises(moe.MoeError, match="elements"):
+        moe.moe_route_compact(z((2, 6), i32), None, 8, out=(z(8, i32), z(8, i32), z(12, i32), z(12, i32)))
+    x, w1, w2 = z((2, 64), bf16), z((3, 256, 64), bf16), z((3, 64, 128), bf16)
+    c, o, r = z(3, i32), z(4, i32), z(12, i32)
+    moe_args = dict(K=6, counts=c, offsets=o, row_to_slot=r)
+    with pytest.raises(moe.MoeError, match="shape"):
+        moe.moe_grouped_ffn(x, w1=z((3, 200, 64), bf16), w2=w2, **moe_args)  # W1 rows != 2F
+    with pytest.raises(moe.MoeError, match="shape"):
+        moe.moe_grouped_ffn(z((2, 32), bf16), w1=w1, w2=w2, **moe_args)      # x width != H
+    with pytest.raises(moe.MoeError, match="dtype"):
+        moe.moe_grouped_ffn(x, w1=w1, w2=z((3, 64, 128), f32), **moe_args)   # mixed weight dtypes
+    with pytest.raises(moe.MoeError, match="elements"):
+        moe.moe_grouped_ffn(x, w1=w1, w2=w2, y=z((4, 64), bf16), **moe_args)  # y rows < T*K
+    with pytest.raises(moe.MoeError, match="scale"):
+        moe.moe_grouped_ffn(x, w1=z((3, 256, 32), u8), w2=z((3, 64, 64), u8), **moe_args)
+    with pytest.raises(moe.MoeError, match="elements"):
+        moe.moe_grouped_ffn_noalloc(x, w1=w1, w2=w2, K=6, counts=z(2, i32), offsets=o, row_to_slot=r)
+    with pytest.raises(moe.MoeError, match="elements"):
+        moe.moe_combine(z((12, 64), bf16), z((2, 6), f32), z(11, i32))         # slot_to_row short
+    with pytest.raises(moe.MoeError, match="dtype"):
+        moe.moe_combine(z((12, 64), bf16), z((2, 6), torch.float64), z(12, i32))
+    with pytest.raises(moe.MoeError, match="shape"):
+        moe.moe_fused_experts(x, z((2, 6), i32), z((3, 6), f32), w1, w2)      # weights [T, K]
+    with pytest.raises(moe.MoeError, match="shape"):
+        moe.moe_pack_ffn_weights(z((3, 256, 64), bf16), z((3, 64, 96), bf16))

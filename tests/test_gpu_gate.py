@@ -34,6 +34,7 @@ def check_gate(logits_host, dtype, K, renorm, tag="", scoring="softmax"):
     # flush, so they only have to lie within that of the exact value
     err = np.abs(w - w_ref) - 2.0 ** -126
     rel = np.max(np.maximum(err, 0.0) / np.abs(w_ref))
+    print(f"[gate] {scoring} {tag} E={E} K={K}: max relative weight error {rel:.3e} (bound {W_RTOL})", flush=True)
     assert rel <= W_RTOL, f"weights rel err {rel:.3e}"
     return rel
 
@@ -56,7 +57,7 @@ def test_gate_expert_counts_bf16(E):
     rng = np.random.default_rng(E)
     for K in sorted({min(E, k) for k in (1, 2, 6, 8, 9, 32)}):
         for T in (1, 7, 333):
-            logits = synth.gate_logits_bf16(T, E, seed=E * 100 + K, tie_fraction=0.3)
+            logits = synth.gate_logits_bf16(T, E, seed=E * 100 + K, tie_fraction=0.3, K=K)
             check_gate(logits, "bf16", K, bool(rng.integers(2)), "sweep")
 
 
@@ -128,7 +129,7 @@ def test_sigmoid_gate_full(E, renorm):
 def test_sigmoid_gate_sweep(E):
     rng = np.random.default_rng(500 + E)
     for K in sorted({min(E, k) for k in (1, 2, 6, 8, 9, 32)}):
-        logits = synth.gate_logits_bf16(97, E, seed=E * 7 + K, tie_fraction=0.3)
+        logits = synth.gate_logits_bf16(97, E, seed=E * 7 + K, tie_fraction=0.3, K=K)
         check_gate(logits, "bf16", K, bool(rng.integers(2)), "sweep", "sigmoid")
         f = (rng.integers(-4, 5, size=(61, E)) * 0.5).astype(np.float32)
         check_gate(f, "f32", K, bool(K % 2), "f32ties", "sigmoid")

@@ -205,3 +205,31 @@ def test_decode_weights_selects_the_storage_format():
     assert np.array_equal(oracle.decode_weights(bits, None, "bf16", 0), [[1.5, -2.0]])
     f = np.array([[[0.25, -3.0]]], dtype=np.float32)
     assert np.array_equal(oracle.decode_weights(f, None, "f32", 0), [[0.25, -3.0]])
+
+
+def test_top1_unit_weight_layer_is_a_dense_swiglu_ffn():
+    # With K = 1, weight 1 and every expert local, the whole layer reduces to
+    # the textbook SwiGLU FFN of each token's expert:
+    #   out[t][i] = sum_f W2[e][i][f] * silu(sum_h W1[e][f][h] x[t][h])
+    #                                 * (sum_h W1[e][F+f][h] x[t][h])
+    # written out here with scalar loops and math.exp, independent of the
+    # oracle's matrix formulation.
+    rng = np.random.default_rng(11)
+    T, E, H, F = 7, 3, 8, 4
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    w1 = (0.3 * rng.standard_normal((E, 2 * F, H))).astype(np.float32)
+    w2 = (0.3 * rng.standard_normal((E, H, F))).astype(np.float32)
+    ids = np.array([[0], [2], [1], [2], [2], [0], [1]], dtype=np.int32)
+    c = synth.MoECase(name="dense", T=T, E_global=E, E_local=E, K=1, H=H, F=F, renormalize=False,
+                      x_dtype="f32", w_dtype="f32", out_dtype="f32", x=x, w1=w1, w2=w2,
+                      topk_ids=ids, topk_weights=np.ones((T, 1), np.float32))
+    out = oracle.moe_layer(c)["out"]
+    for t in range(T):
+        e = int(ids[t, 0])
+        for i in range(H):
+            acc = 0.0
+            for f in range(F):
+                g = sum(float(w1[e, f, h]) * float(x[t, h]) for h in range(H))
+                u = sum(float(w1[e, F + f, h]) * float(x[t, h]) for h in range(H))
+                acc += float(w2[e, i, f]) * (g / (1.0 + math.exp(-g))) * u
+            assert out[t, i] == pytest.approx(acc, rel=1e-12, abs=1e-14)

@@ -40,3 +40,17 @@ def test_mxfp4_case_shapes_and_scale_range():
     assert c.w1_scale.min() >= 119 and c.w1_scale.max() <= 127
     for t in range(16):
         assert len(set(c.topk_ids[t].tolist())) == 8
+
+
+def test_gate_case_has_boundary_ties():
+    # half of the ~1% injected rows tie exactly at the K-th place: the value
+    # ranked K-th equals the value ranked (K+1)-th
+    T, E, K = 65536, 128, 8
+    c = synth.gate_case(E, T=T, K=K, seed=0)
+    f = (c.logits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    srt = -np.sort(-f, axis=1)
+    boundary = int(np.count_nonzero(srt[:, K - 1] == srt[:, K]))
+    injected = int(round(T * 0.01))
+    assert boundary >= injected // 2
+    top = int(np.count_nonzero(srt[:, 0] == srt[:, 1]))
+    assert top >= injected // 2
