@@ -16,10 +16,14 @@ is replayed untimed for 0.1 s first.
 
 Besides the contract fields the line carries:
   roofline      the grouped FFN call (GEMM1 + silu_and_mul kernel and GEMM2
-                kernel): algorithmic HBM bytes per call over its duration from
-                HIP events on the launch stream, against 8 TB/s (its 256
-                flop/byte lies below the bf16 ridge of ~312, so HBM bounds it);
-                the MFMA rate against the 2.5 PFLOP/s dense peak rides along
+                kernel): its algorithmic flops over its duration from HIP
+                events on the launch stream, against the 2.5 PFLOP/s dense
+                bf16 matrix-core peak (the bar this call is held to); the HBM
+                rate on its minimum bytes (weights + x) and on the bytes with
+                the act / y hand-over rides along, and both against the
+                measured peaks
+  measured_peaks  what this GPU achieves in the same run: a 2 GiB streaming
+                read, a 1 GiB copy and a bf16 MFMA loop (library probes)
   cpu_baseline  the fp64 CPU oracle on a bounded token sample of the same
                 workload, on this host's cores
   breakdown     per-call milliseconds of the step
@@ -64,7 +68,8 @@ def parse():
                    help="only run a plain device-to-device copy of MIB MiB five times (the reference kernel "
                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exit")
     p.add_argument("--profile", default="", metavar="WHAT",
-                   help="only run one secondary for a kernel trace and exit: 'gate' (the five gate "
+                   help="only run one secondary for a kernel trace and exit: 'peaks' (the read, copy and "
+                        "MFMA probes), 'gate' (the five gate "
                         "configurations), 'decode:PATTERN' (one decode route pattern, every path) or "
                         "'mxfp4[:T<n>_<routes>]' (the MXFP4 weight-streaming cases)")
     return p.parse_args()
@@ -248,16 +253,23 @@ def bench_prefill(args, dev):
     row_bytes = N * (2 * F * 2 + H * 2)              # act written + read, y written (bf16)
     x_bytes = T * H * 2                              # each token's x once
     alg_bytes = weight_bytes + row_bytes + x_bytes
+    min_bytes = weight_bytes + x_bytes               # what must cross HBM at least once
     ffn_s = per["grouped_ffn"] / 1000.0
-    gbs = alg_bytes / ffn_s / 1e9
     tflops = flops / ffn_s / 1e12
+    # The bar for this call is stated against the bf16 matrix-core peak, so
+    # the roofline is the MFMA one; the HBM view rides along, on the minimum
+    # bytes (every expert's weights and each token's x once) and on the
+    # bytes including the act and y rows the two kernels hand over.
     roofline = {
-        "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_for("grouped_ffn_prefill"),
+        "bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": traffic_for("grouped_ffn_prefill"),
         "kernel": "moe_grouped_ffn (ffn_tiled_kernel: GEMM1 + silu_and_mul, then GEMM2)",
-        "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_ms": round(per["grouped_ffn"], 4),
-        "mfma_tflops": round(tflops, 1), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
-        "algorithmic_flops_per_launch": flops,
+        "algorithmic_flops_per_launch": flops, "avg_launch_ms": round(per["grouped_ffn"], 4),
+        "hbm": {"min_bytes_per_launch": min_bytes, "min_bytes_gbs": round(min_bytes / ffn_s / 1e9, 1),
+                "min_bytes_frac": round(min_bytes / ffn_s / 1e9 / HBM_PEAK_GBS, 4),
+                "with_act_y_bytes_per_launch": alg_bytes,
+                "with_act_y_gbs": round(alg_bytes / ffn_s / 1e9, 1),
+                "with_act_y_frac": round(alg_bytes / ffn_s / 1e9 / HBM_PEAK_GBS, 4)},
     }
     log(f"[bench] prefill layer: {ms_per_step:.3f} ms/step, {T / (ms_per_step / 1e3):.0f} tokens/s; "
         + ", ".join(f"{n} {v:.3f} ms" for n, v in per.items()))
@@ -326,8 +338,67 @@ def bench_gate(dev, E, reps, scoring="softmax"):
     ms = graph_ms(calls, max(1, reps // nbuf), dev) / nbuf
     nbytes = T * E * 2 + T * K * 12
     gbs = nbytes / (ms / 1e3) / 1e9
-    return {"scoring": scoring, "E": E, "T": T, "K": K, "ms": round(ms, 5), "mrows_per_s": round(T / (ms / 1e3) / 1e6, 1),
-            "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_call": nbytes}
+    res = {"scoring": scoring, "E": E, "T": T, "K": K, "ms": round(ms, 5), "mrows_per_s": round(T / (ms / 1e3) / 1e6, 1),
+           "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_call": nbytes}
+    if scoring == "softmax":
+        # the same loads and stores without the selection: this access
+        # pattern's ceiling, timed the same way
+        def loads_only():
+            for b in bufs:
+                moe.moe_probe_gate_loads(b[0], K, b[1], b[2], b[3])
+
+        ms0 = graph_ms(loads_only, max(1, reps // nbuf), dev) / nbuf
+        res["load_only_ms"] = round(ms0, 5)
+        res["load_only_hbm_frac"] = round(nbytes / (ms0 / 1e3) / 1e9 / HBM_PEAK_GBS, 4)
+    return res
+
+
+def measured_peaks(dev):
+    """What this GPU achieves, next to the spec peaks: a streaming read of
+    2 GiB and a 1 GiB -> 1 GiB copy (both larger than the 256 MB last-level
+    cache; HIP events around each call, median of 10), and a bf16 MFMA loop
+    (4 independent 32x32x16 MFMAs per round on register operands, 8192 waves;
+    median of 10 calls of ~4 ms) at the clock the chip runs under that load."""
+    import statistics
+
+    import torch
+
+    import mixture_experts_routing_amd as moe
+
+    def timed(fn, n=10):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        s = torch.cuda.current_stream(dev)
+        ts = []
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(s)
+            fn()
+            b.record(s)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return statistics.median(ts)
+
+    rd = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    rd.fill_(1)
+    out = torch.empty(4096 * 256, dtype=torch.int32, device=dev)
+    t_read = timed(lambda: moe.moe_probe_read(rd, out))
+    del rd
+    src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: moe.moe_probe_copy(src, dst))
+    del src, dst
+    blocks, iters = 2048, 8000
+    mo = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    t_mfma = timed(lambda: moe.moe_probe_mfma(iters, blocks, mo))
+    flops = blocks * 4 * iters * 4 * 32768
+    return {"read_gbs": round((2 << 30) / (t_read / 1e3) / 1e9, 1),
+            "copy_gbs": round(2 * (1 << 30) / (t_copy / 1e3) / 1e9, 1),
+            "mfma_bf16_tflops": round(flops / (t_mfma / 1e3) / 1e12, 1),
+            "spec": {"hbm_gbs": HBM_PEAK_GBS, "mfma_bf16_tflops": BF16_PEAK_TFLOPS},
+            "probes": "moe_probe_read (2 GiB), moe_probe_copy (1 GiB -> 1 GiB, bytes read + written), "
+                      "moe_probe_mfma (2048 x 256 threads, 8000 rounds of 4 MFMAs)"}
 
 
 # ---------------------------------------------------------------------------
@@ -626,7 +697,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
         return
     if args.profile:
-        if args.profile == "gate":
+        if args.profile == "peaks":
+            res = measured_peaks(dev)
+        elif args.profile == "gate":
             res = [bench_gate(dev, E, 64) for E in (128, 160)]
             res += [bench_gate(dev, E, 64, "sigmoid") for E in (128, 160, 256)]
         elif args.profile.startswith("decode:"):
@@ -639,13 +712,22 @@ def main():
         return
     c, ms, per, roofline, settle, gate_fusion = bench_prefill(args, dev)
     secondary = {"prefill_gate_compaction": gate_fusion}
+    peaks = measured_peaks(dev)
+    log(f"[bench] measured peaks: read {peaks['read_gbs']} GB/s, copy {peaks['copy_gbs']} GB/s, "
+        f"bf16 MFMA loop {peaks['mfma_bf16_tflops']} TFLOP/s")
+    roofline["measured_peak"] = peaks["mfma_bf16_tflops"]
+    roofline["frac_of_measured_peak"] = round(roofline["achieved"] / peaks["mfma_bf16_tflops"], 4)
+    roofline["hbm"]["min_bytes_frac_of_measured_read"] = round(roofline["hbm"]["min_bytes_gbs"] / peaks["read_gbs"], 4)
     if not args.no_secondary:
         reps = 50 if args.quick else 400
         secondary["gate"] = [bench_gate(dev, E, reps) for E in (128, 160)]
         secondary["gate"] += [bench_gate(dev, E, reps, "sigmoid") for E in (128, 160, 256)]
         for g in secondary["gate"]:
+            g["hbm_frac_of_measured_read"] = round(g["gbs"] / peaks["read_gbs"], 4)
             log(f"[bench] gate {g['scoring']} E={g['E']}: {g['ms'] * 1e3:.2f} us, {g['mrows_per_s']} Mrows/s, "
-                f"{g['gbs']} GB/s ({100 * g['hbm_frac']:.1f}% of HBM)")
+                f"{g['gbs']} GB/s ({100 * g['hbm_frac']:.1f}% of HBM)"
+                + (f"; loads only {g['load_only_ms'] * 1e3:.2f} us ({100 * g['load_only_hbm_frac']:.1f}%)"
+                   if "load_only_ms" in g else ""))
         secondary["decode"] = bench_decode(dev, 5 if args.quick else 20)
         secondary["mxfp4"] = bench_mxfp4(dev, 5 if args.quick else 20)
         secondary["route_align"] = bench_align(dev, 5 if args.quick else 20)
@@ -665,7 +747,8 @@ def main():
         "config": {"workload": "prefill_moe_layer", "tokens": c.T, "experts": c.E_local, "top_k": c.K,
                    "renormalize": True, "hidden": c.H, "expert_ffn": c.F, "weights": "bf16 (tile-packed layout)",
                    "parallelism": "single-gpu"},
-        "roofline": roofline, "cpu_baseline": cpu, "breakdown_ms": {k: round(v, 4) for k, v in per.items()},
+        "roofline": roofline, "cpu_baseline": cpu, "measured_peaks": peaks,
+        "breakdown_ms": {k: round(v, 4) for k, v in per.items()},
         "secondary": secondary,
     }
     print(json.dumps(line), flush=True)

@@ -304,6 +304,35 @@ size_t moe_fused_experts_workspace_bytes(int64_t T, int32_t K, int32_t H, int32_
                                          int w_dtype);
 
 /*
+ * Measurement probes -- not steps of the layer.  Each runs one kernel of a
+ * known access pattern or instruction mix, so that a benchmark can report
+ * what this GPU achieves next to the spec peaks the roofline uses, and the
+ * ceiling of the gate's own memory traffic.
+ *
+ * moe_probe_read: reads bytes of src once (16-byte non-temporal loads, 4096
+ *   blocks x 256 threads, grid-stride); each thread folds what it read into
+ *   out[thread], so out needs out_words >= 4096*256 (MOE_ERR_WORKSPACE
+ *   otherwise).  bytes % 16 == 0, src 16-byte aligned.
+ * moe_probe_copy: copies bytes from src to dst with the same loads and
+ *   non-temporal stores.  bytes % 16 == 0, both 16-byte aligned.
+ * moe_probe_mfma: blocks x 256 threads; every wave issues iters rounds of
+ *   four independent v_mfma_f32_32x32x16_bf16 on register operands
+ *   (4 x 32768 flops per round); out[blocks*256] receives the sums.
+ * moe_probe_gate_loads: the memory traffic of moe_topk_softmax's bf16 kernel
+ *   for E = 8V, V in {8, 12, 16, 20, 24}, K <= 8 (the same grid, per-lane
+ *   loads of the row's logits and K stores of weight, id and token-expert
+ *   index per row) without its sort, selection or softmax; the values it
+ *   stores are not a gate's.  Source of the access pattern: page "Upstream
+ *   Reference: Deep-Spark xllm + vllm", section "Call Chain: MoE topk_softmax
+ *   on BI-V100" (the op's inputs and outputs).
+ */
+int moe_probe_read(const void* src, size_t bytes, uint32_t* out, size_t out_words, void* stream);
+int moe_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
+int moe_probe_mfma(int64_t iters, int32_t blocks, float* out, void* stream);
+int moe_probe_gate_loads(const void* logits, int64_t T, int32_t E, int32_t K, float* topk_weights,
+                         int32_t* topk_ids, int32_t* token_expert_indices, void* stream);
+
+/*
  * moe_pack_ffn_weights -- store bf16 expert weights in the tile-packed layout
  * (MOE_BF16_TILED) that the many-rows-per-expert FFN kernels stream with
  * contiguous loads.  A one-time transform of the weights (model load), not

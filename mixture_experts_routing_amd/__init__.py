@@ -20,6 +20,7 @@ _LIB = _lib.load()
 __all__ = [
     "moe_topk_softmax", "moe_topk_sigmoid", "moe_route_compact", "moe_route_align", "moe_grouped_ffn",
     "moe_grouped_ffn_noalloc", "moe_grouped_ffn_control", "moe_fused_experts", "moe_topk_compact", "moe_combine", "moe_pack_ffn_weights", "moe_layer",
+    "moe_probe_read", "moe_probe_copy", "moe_probe_mfma", "moe_probe_gate_loads",
     "MOE_F32", "MOE_BF16", "MOE_MXFP4", "MOE_BF16_TILED", "MoeError", "library_path",
 ]
 
@@ -468,3 +469,43 @@ def moe_layer(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, K: int, logit
     out = moe_combine(y, topk_weights, s2r, out_dtype=out_dtype or x.dtype, stream=stream)
     return dict(topk_weights=topk_weights, topk_ids=topk_ids, token_expert_indices=tei, counts=counts,
                 offsets=offsets, slot_to_row=s2r, row_to_slot=r2s, y=y, out=out)
+
+
+# ---------------------------------------------------------------------------
+# measurement probes (not steps of the layer): see include/moe_routing.h
+
+
+def moe_probe_read(src: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    """Read every byte of src once (streaming read); out: uint32 [4096*256]."""
+    _req(out, "out", torch.int32, 4096 * 256)
+    dev = _dev(src, out)
+    _check(_LIB.moe_probe_read(_ptr(src), _nbytes(src), _ptr(out), out.numel(), _stream(stream, dev)),
+           "moe_probe_read")
+
+
+def moe_probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """Copy src into dst (same byte size)."""
+    if _nbytes(dst) < _nbytes(src):
+        raise MoeError("dst smaller than src")
+    dev = _dev(src, dst)
+    _check(_LIB.moe_probe_copy(_ptr(src), _ptr(dst), _nbytes(src), _stream(stream, dev)), "moe_probe_copy")
+
+
+def moe_probe_mfma(iters: int, blocks: int, out: torch.Tensor, stream=None) -> None:
+    """blocks x 256 threads, each wave iters rounds of 4 bf16 32x32x16 MFMAs; out: f32 [blocks*256]."""
+    _req(out, "out", _F32, blocks * 256)
+    dev = _dev(out)
+    _check(_LIB.moe_probe_mfma(iters, blocks, _ptr(out), _stream(stream, dev)), "moe_probe_mfma")
+
+
+def moe_probe_gate_loads(logits: torch.Tensor, K: int, topk_weights: torch.Tensor, topk_ids: torch.Tensor,
+                         token_expert_indices: Optional[torch.Tensor] = None, stream=None) -> None:
+    """The bf16 gate's loads and stores without its selection (load-only ceiling)."""
+    _req(logits, "logits", _BF16, ndim=2)
+    T, E = logits.shape
+    _req(topk_weights, "topk_weights", _F32, T * K)
+    _req(topk_ids, "topk_ids", _I32, T * K)
+    _req(token_expert_indices, "token_expert_indices", _I32, T * K)
+    dev = _dev(logits, topk_weights, topk_ids, token_expert_indices)
+    _check(_LIB.moe_probe_gate_loads(_ptr(logits), T, E, K, _ptr(topk_weights), _ptr(topk_ids),
+                                     _ptr(token_expert_indices), _stream(stream, dev)), "moe_probe_gate_loads")

@@ -41,6 +41,10 @@ SIGNATURES = {
     "moe_fused_experts": (_int, [_p, _int, _i64, _i32, _i32, _i32, _p, _p, _p, _i32, _i32, _p, _p, _p, _p, _int,
                                  _p, _p, _p, _p, _p, _int, _p, _sz, _p]),
     "moe_fused_experts_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i32, _int]),
+    "moe_probe_read": (_int, [_p, _sz, _p, _sz, _p]),
+    "moe_probe_copy": (_int, [_p, _p, _sz, _p]),
+    "moe_probe_mfma": (_int, [_i64, _i32, _p, _p]),
+    "moe_probe_gate_loads": (_int, [_p, _i64, _i32, _i32, _p, _p, _p, _p]),
     "moe_status_string": (ctypes.c_char_p, [_int]),
     "moe_last_hip_error": (_int, []),
     "moe_version": (ctypes.c_char_p, []),

@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
 SOURCES = ["moe_api.hip", "topk_softmax.hip", "route_compact.hip", "grouped_ffn.hip", "grouped_ffn_tiled.hip",
-           "combine.hip"]
+           "combine.hip", "probes.hip"]
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32
 HIPCC_FLAGS = [

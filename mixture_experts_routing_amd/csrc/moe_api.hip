@@ -318,6 +318,35 @@ int moe_pack_ffn_weights(const void* w1, const void* w2, int32_t E_local, int32_
                                                  static_cast<uint16_t*>(w2_tiled), static_cast<hipStream_t>(stream)));
 }
 
+int moe_probe_read(const void* src, size_t bytes, uint32_t* out, size_t out_words, void* stream) {
+  if (bytes == 0) return MOE_OK;
+  if (!src || !out || bytes % 16 != 0 || !aligned(src, 16)) return MOE_ERR_INVALID_ARG;
+  if (out_words < (size_t)moe::probe_read_out_words()) return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_probe_read(src, (int64_t)bytes, out, static_cast<hipStream_t>(stream)));
+}
+
+int moe_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (bytes == 0) return MOE_OK;
+  if (!src || !dst || bytes % 16 != 0 || !aligned(src, 16) || !aligned(dst, 16)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_probe_copy(src, dst, (int64_t)bytes, static_cast<hipStream_t>(stream)));
+}
+
+int moe_probe_mfma(int64_t iters, int32_t blocks, float* out, void* stream) {
+  if (iters < 1 || blocks < 1 || !out) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_probe_mfma(iters, blocks, out, static_cast<hipStream_t>(stream)));
+}
+
+int moe_probe_gate_loads(const void* logits, int64_t T, int32_t E, int32_t K, float* topk_weights,
+                         int32_t* topk_ids, int32_t* token_expert_indices, void* stream) {
+  if (T < 0 || K < 1 || K > 8 || K > E) return MOE_ERR_INVALID_ARG;
+  const int V = E / 8;
+  if (E % 8 != 0 || (V != 8 && V != 12 && V != 16 && V != 20 && V != 24)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_weights || !topk_ids || !aligned(logits, 16)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_probe_gate_loads(static_cast<const uint16_t*>(logits), T, E, K, topk_weights,
+                                                 topk_ids, token_expert_indices, static_cast<hipStream_t>(stream)));
+}
+
 int moe_combine(const void* y, int y_dtype, const float* topk_weights, const int32_t* slot_to_row, int64_t T,
                 int32_t K, int32_t H, void* out, int out_dtype, void* stream) {
   if (T < 0 || K < 1 || H < 1) return MOE_ERR_INVALID_ARG;

@@ -260,4 +260,12 @@ hipError_t launch_fused_experts(const uint16_t* x, int64_t T, int K, int H, int 
 hipError_t launch_combine(const void* y, int y_dtype, const float* w, const int32_t* slot_to_row,
                           int64_t T, int K, int H, void* out, int out_dtype, hipStream_t stream);
 
+// measurement probes (no step of the layer)
+hipError_t launch_probe_read(const void* src, int64_t bytes, uint32_t* out, hipStream_t stream);
+hipError_t launch_probe_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+hipError_t launch_probe_mfma(int64_t iters, int blocks, float* out, hipStream_t stream);
+hipError_t launch_probe_gate_loads(const uint16_t* logits, int64_t T, int E, int K, float* w, int32_t* ids,
+                                   int32_t* tei, hipStream_t stream);
+int probe_read_out_words();
+
 }  // namespace moe
