@@ -512,11 +512,14 @@ __device__ __forceinline__ bf16x8 widen_mx8(uint32_t w, uint32_t e8) {
 // The x (or act) operand takes the same elements, so each K element meets its
 // weight exactly once; only the order of the sum differs from unit by unit.
 // The weight loads of all NB batches are issued before the first MFMA, so a
-// wave keeps 1 KB of codes per batch in flight (up to 8 KB).
-template <int NB>
-__device__ __forceinline__ void mx_batches(f32x4& acc, const uint16_t* __restrict__ xr,
-                                           const uint8_t* __restrict__ wrow, const uint8_t* __restrict__ srow, int u,
-                                           int g) {
+// wave keeps 1 KB of codes per batch in flight (up to 8 KB).  TWO (a 32-row
+// tile): the A rows of the second 16-row half (xr1) meet the same widened
+// weights, so one weight byte feeds two MFMAs.  Unit v of an A row starts at
+// element 32 (v - ub) of xr0 / xr1.
+template <int NB, bool TWO>
+__device__ __forceinline__ void mx_batches(f32x4& acc0, f32x4& acc1, const uint16_t* __restrict__ xr0,
+                                           const uint16_t* __restrict__ xr1, const uint8_t* __restrict__ wrow,
+                                           const uint8_t* __restrict__ srow, int u, int ub, int g) {
   u32x4 cw[NB];
   uint32_t sc[NB];
 #pragma unroll
@@ -526,19 +529,24 @@ __device__ __forceinline__ void mx_batches(f32x4& acc, const uint16_t* __restric
   }
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    const uint16_t* xp = xr + 32 * (u + 4 * b + g);
-    bf16x8 xa[4];
+    const int xo = 32 * (u + 4 * b + g - ub);
+    bf16x8 xa[4], xb[TWO ? 4 : 1];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xa[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xp + 8 * j));
+    for (int j = 0; j < 4; ++j) xa[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xr0 + xo + 8 * j));
+    if constexpr (TWO) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j], widen_mx8(cw[b][j], sc[b]), acc, 0, 0, 0);
+      for (int j = 0; j < 4; ++j)
+        xb[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xr1 + xo + 8 * j));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 wv = widen_mx8(cw[b][j], sc[b]);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j], wv, acc0, 0, 0, 0);
+      if constexpr (TWO) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb[j], wv, acc1, 0, 0, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);  // the next batch's x loads stay after these MFMAs
   }
 }
-
-
-
 
 __device__ __forceinline__ bf16x8 unit_bf16(const uint16_t* __restrict__ row, int u, int g) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + 32 * u + 8 * g));
@@ -576,85 +584,184 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// One wave's share of a decode item: the dot products of the 16 A rows (xr:
-// this lane's row, bf16) with the 16 weight rows (rw: this lane's row) over K
-// units [u, u_end).  xr may point into LDS (staged rows) or global memory.
-template <bool MX, int U>
-__device__ __forceinline__ f32x4 tile_dot(const uint16_t* __restrict__ xr, const void* __restrict__ w,
-                                          const uint8_t* __restrict__ ws, int64_t rw, int kdim, int u, int u_end,
-                                          int g) {
-  f32x4 acc = {0, 0, 0, 0};
+// One wave's share of a decode item: the dot products of the tile's A rows
+// (xr0: this lane's row c; xr1: row 16 + c, used when TWO) with the 16 weight
+// rows (rw: this lane's weight row) over K units [u, u_end), added to acc0 /
+// acc1 in unit order.  Unit v of an A row starts at element 32 (v - ub): the
+// rows may sit in LDS (a staged chunk that begins at unit ub) or in global
+// memory (ub = 0).  A 32-row tile reads each weight byte once for both
+// halves (the weight pass of a tile serves all its rows).
+template <bool MX, int U, bool TWO>
+__device__ __forceinline__ void tile_dot(f32x4& acc0, f32x4& acc1, const uint16_t* __restrict__ xr0,
+                                         const uint16_t* __restrict__ xr1, int ub, const void* __restrict__ w,
+                                         const uint8_t* __restrict__ ws, int64_t rw, int kdim, int u, int u_end,
+                                         int g) {
   if constexpr (MX) {
     const uint8_t* wrow = static_cast<const uint8_t*>(w) + rw * (kdim / 2);
     const uint8_t* srow = ws + rw * (kdim / 32);
-    for (; u + 32 <= u_end; u += 32) mx_batches<8>(acc, xr, wrow, srow, u, g);
-    if (u + 16 <= u_end) {
-      mx_batches<4>(acc, xr, wrow, srow, u, g);
-      u += 16;
-    }
+    // TWO: batches of at most 4 (the second A half needs the registers)
+    if constexpr (!TWO)
+      for (; u + 32 <= u_end; u += 32) mx_batches<8, TWO>(acc0, acc1, xr0, xr1, wrow, srow, u, ub, g);
+    for (; u + 16 <= u_end; u += 16) mx_batches<4, TWO>(acc0, acc1, xr0, xr1, wrow, srow, u, ub, g);
     if (u + 8 <= u_end) {
-      mx_batches<2>(acc, xr, wrow, srow, u, g);
+      mx_batches<2, TWO>(acc0, acc1, xr0, xr1, wrow, srow, u, ub, g);
       u += 8;
     }
     if (u + 4 <= u_end) {
-      mx_batches<1>(acc, xr, wrow, srow, u, g);
+      mx_batches<1, TWO>(acc0, acc1, xr0, xr1, wrow, srow, u, ub, g);
       u += 4;
     }
   } else {
-    for (; u + U <= u_end; u += U) {
-      WUnit<MX> b[U];
-      bf16x8 a[U];
+    constexpr int V = TWO ? U / 2 : U;  // the second A half takes the registers of half the batch
+    for (; u + V <= u_end; u += V) {
+      WUnit<MX> b[V];
+      bf16x8 a[V], a1[TWO ? V : 1];
 #pragma unroll
-      for (int j = 0; j < U; ++j) b[j].load(w, ws, rw, kdim, u + j, g);
+      for (int j = 0; j < V; ++j) b[j].load(w, ws, rw, kdim, u + j, g);
 #pragma unroll
-      for (int j = 0; j < U; ++j) a[j] = unit_bf16(xr, u + j, g);
+      for (int j = 0; j < V; ++j) a[j] = unit_bf16(xr0, u + j - ub, g);
+      if constexpr (TWO) {
 #pragma unroll
-      for (int j = 0; j < U; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], b[j].get(), acc, 0, 0, 0);
+        for (int j = 0; j < V; ++j) a1[j] = unit_bf16(xr1, u + j - ub, g);
+      }
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], b[j].get(), acc0, 0, 0, 0);
+        if constexpr (TWO) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[j], b[j].get(), acc1, 0, 0, 0);
+      }
     }
   }
   for (; u < u_end; ++u) {
     WUnit<MX> b;
     b.load(w, ws, rw, kdim, u, g);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unit_bf16(xr, u, g), b.get(), acc, 0, 0, 0);
+    const bf16x8 wv = b.get();
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unit_bf16(xr0, u - ub, g), wv, acc0, 0, 0, 0);
+    if constexpr (TWO) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unit_bf16(xr1, u - ub, g), wv, acc1, 0, 0, 0);
   }
-  return acc;
 }
 
+// The same for one 16-row tile whose rows are in global memory.
+template <bool MX, int U>
+__device__ __forceinline__ f32x4 tile_dot16(const uint16_t* __restrict__ xr, const void* __restrict__ w,
+                                            const uint8_t* __restrict__ ws, int64_t rw, int kdim, int u, int u_end,
+                                            int g) {
+  f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+  tile_dot<MX, U, false>(acc0, acc1, xr, xr, 0, w, ws, rw, kdim, u, u_end, g);
+  return acc0;
+}
+
+// Tile height of the decode kernels: up to 32 rows of one expert share every
+// weight byte an item streams (two 16-row MFMA halves), so an expert with up
+// to 32 rows is one weight pass.
+constexpr int kDecBM = 32;
+
 // Staged A rows of a decode item.  When the splits leave several waves of a
-// block on the same K range, those waves would each load the same 16 A rows
+// block on the same K range, those waves would each load the same A rows
 // from global memory; instead the block copies the item's distinct rows (at
-// most 16, rows past the tile's end use row 0) into LDS once, with
-// contiguous 16-byte loads, and every wave reads its fragments from there.
-// The copy and its two barriers pay off with at least 4 waves per range
-// (S <= 4), or 2 per range (S = 8) when the tile holds 8 rows or more.  Only
-// the MXFP4 kernels stage: their A rows are 4x the bytes of the weight codes
-// they meet, and the 128 KB block they need keeps a kernel's blocks from
-// sharing a compute unit with the previous kernel's, which costs the bf16
-// decode kernels more than the staging saves them.
-// Row r sits at r * (2 K + kXsPad) bytes, an odd multiple of 16 (K is a
-// multiple of 32), so the 16 rows start in 16 distinct 16-byte slots of the
-// 256-byte bank period and the 16 lanes of a quarter-wave (16 rows, one
-// piece) hit distinct banks.
-constexpr int kXsMaxK = 4096;  // longest reduction whose rows are staged
+// most 32; rows past the tile's end use row 0) into LDS, with contiguous
+// 16-byte loads, and every wave reads its fragments from there.  The copy
+// and its barriers pay off with at least 4 waves per range (S <= 4), or 2 per
+// range (S = 8) when the tile holds 8 rows or more.  Only the MXFP4 kernels
+// stage: their A rows are 4x the bytes of the weight codes they meet, and
+// the 128 KB block they need keeps a kernel's blocks from sharing a compute
+// unit with the previous kernel's, which costs the bf16 decode kernels more
+// than the staging saves them.
+// Rows that do not fit whole (n rows x K elements above kXsBytes: 32 rows at
+// K > 2048, 16 rows at K > 4096) are staged in chunks of whole K units; every
+// split takes its share of each chunk (split ks: the ks-th of S equal parts),
+// so no wave waits idle while a chunk is in LDS.  In a chunk of nu units, row
+// r sits at r * (64 nu + kXsPad) bytes, an odd multiple of 16, so the 16 rows
+// a quarter-wave reads (one piece each) start in 16 distinct 16-byte slots of
+// the 256-byte bank period and hit distinct banks.
 constexpr int kXsPad = 16;
-constexpr int kXsBytes = 16 * (2 * kXsMaxK + kXsPad);
+constexpr int kXsBytes = 32 * (64 * 64 + kXsPad);  // 32 rows x 2048 elements (or 16 rows x 4096)
+constexpr int kRedBytes = kDecWaves * 8 * 64 * 4;  // split partials: 2 x 4 floats per lane per wave
+static_assert(kXsBytes >= kRedBytes, "the split partials reuse the staging buffer");
 
 __device__ __forceinline__ bool stage_item(int S, int nrows) { return S <= 4 || (S <= 8 && nrows >= 8); }
 
-// Copy rows [0, n) of an item (row r from src_row(r), K elements each) into
-// xs, then a barrier (the rows are visible).  Every thread of the block takes
-// part; the caller has passed a barrier after the previous item's reads.
+// K units per staged chunk for n rows of `units` units: all of them if they
+// fit, else the most that fit, a multiple of 4 (the MXFP4 batch).
+__device__ __forceinline__ int stage_chunk_units(int n, int units) {
+  const int kmax = (kXsBytes / n - kXsPad) / 64;
+  return units <= kmax ? units : (kmax & ~3);
+}
+
+// Copy elements [e0, e0 + ne) of rows [0, n) (row r from src_row(r)) into xs
+// at row stride 2 ne + kXsPad bytes, then a barrier (the rows are visible).
+// Every thread of the block takes part; the caller has passed a barrier after
+// the previous reads of xs.
 template <typename SrcRow>
-__device__ __forceinline__ void stage_rows(uint8_t* __restrict__ xs, int n, int kdim, SrcRow src_row) {
-  const int ppr = kdim / 8;  // 16-byte pieces per row
-  const int RS = 2 * kdim + kXsPad;
+__device__ __forceinline__ void stage_rows(uint8_t* __restrict__ xs, int n, int e0, int ne, SrcRow src_row) {
+  const int ppr = ne / 8;  // 16-byte pieces per row
+  const int RS = 2 * ne + kXsPad;
   for (int p = threadIdx.x; p < n * ppr; p += kDecThreads) {
     const int r = p / ppr, q = p - r * ppr;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(src_row(r) + 8 * q);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(src_row(r) + e0 + 8 * q);
     *reinterpret_cast<u32x4*>(xs + r * RS + 16 * q) = v;
   }
   lds_barrier();
 }
+
+// The dot products of one item over its staged rows: the block copies the
+// rows chunk by chunk and each wave adds its split's share of every chunk.
+// `active`, n and the split are wave-uniform.
+template <bool MX, int U, bool TWO, typename SrcRow>
+__device__ __forceinline__ void staged_dot(f32x4& acc0, f32x4& acc1, uint8_t* __restrict__ xs, int n, bool active,
+                                           SrcRow src_row, const void* __restrict__ w,
+                                           const uint8_t* __restrict__ ws, int64_t rw, int kdim, int ks, int S,
+                                           int c, int g) {
+  const int units = kdim / 32;
+  const int kc = stage_chunk_units(n, units);
+  for (int c0 = 0; c0 < units; c0 += kc) {
+    const int nu = min(kc, units - c0);
+    lds_barrier();  // every wave is done with the previous rows in xs
+    stage_rows(xs, n, 32 * c0, 32 * nu, src_row);
+    if (active) {
+      const int pc = (nu + S - 1) / S;
+      const int ub = c0 + min(nu, ks * pc), ue = c0 + min(nu, ks * pc + pc);
+      const int RS = 64 * nu + kXsPad;
+      const uint16_t* x0 = reinterpret_cast<const uint16_t*>(xs + (c < n ? c : 0) * RS);
+      const uint16_t* x1 = reinterpret_cast<const uint16_t*>(xs + (16 + c < n ? 16 + c : 0) * RS);
+      tile_dot<MX, U, TWO>(acc0, acc1, x0, x1, c0, w, ws, rw, kdim, ub, ue, g);
+    }
+  }
+}
+
+// Sum of the S split partials of an item, in split order, into the waves of
+// split 0 (red: kRedBytes of LDS; it may alias the staged rows, so the
+// caller passes `staged` to wait for every wave's last read of them first).
+template <bool TWO>
+__device__ __forceinline__ void split_reduce(f32x4& acc0, f32x4& acc1, float* __restrict__ red, bool staged, int S,
+                                             int ks, int wave, int lane) {
+  if (S <= 1) return;
+  if (staged) lds_barrier();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[(wave * 8 + i) * 64 + lane] = acc0[i];
+  if constexpr (TWO) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[(wave * 8 + 4 + i) * 64 + lane] = acc1[i];
+  }
+  __syncthreads();
+  if (ks == 0) {
+    for (int sp = 1; sp < S; ++sp) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc0[i] += red[((wave + sp) * 8 + i) * 64 + lane];
+      if constexpr (TWO) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc1[i] += red[((wave + sp) * 8 + 4 + i) * 64 + lane];
+      }
+    }
+  }
+  __syncthreads();  // red is rewritten by the next item
+}
+
+// Where a decode item sits: its tile (expert, first grouped row, rows), this
+// wave's column group and K split.  All fields are wave-uniform.
+struct DecItem {
+  int e, row0, nrows, cg, ks, S, u_begin, u_end;
+  bool active, staged;
+};
 
 // Compaction inputs and outputs of the fused GEMM1 (ROUTES = true): every
 // wave derives the route table itself from topk_ids and the expert map, and
@@ -669,6 +776,95 @@ struct FusedRoutes {
   int32_t* r2s;
 };
 
+// GEMM1 + silu_and_mul of one decode item (TWO: a tile of more than 16
+// rows).  inv (ROUTES): lane r holds the slot of grouped row r.
+template <bool MX, bool ROUTES, bool TWO>
+__device__ __forceinline__ void ffn1_item(const DecItem& d, const uint16_t* __restrict__ x, int K, int H, int F,
+                                          const void* __restrict__ w1, const uint8_t* __restrict__ w1s,
+                                          const int32_t* __restrict__ r2s, int inv, uint16_t* __restrict__ act,
+                                          uint8_t* __restrict__ smem, int* __restrict__ xtok) {
+  constexpr int U = dec_unroll1<MX>();
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  // W1 row of this lane's MFMA column: gate row (c < 8) or up row
+  const int64_t rw = (int64_t)d.e * 2 * F + (c >> 3) * F + d.cg * 8 + (c & 7);
+  f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+  if (d.staged) {
+    if (wave == 0) {  // the x row (token) of each of the item's rows
+      const int r = d.row0 + (lane < d.nrows ? lane : 0);
+      int slot;
+      if constexpr (ROUTES) slot = __shfl(inv, r, 64);
+      else slot = r2s[r];
+      if (lane < kDecBM) xtok[lane] = slot / K;
+    }
+    // staged_dot's first barrier makes xtok visible
+    staged_dot<MX, U, TWO>(acc0, acc1, smem, d.nrows, d.active, [&](int r) { return x + (int64_t)xtok[r] * H; }, w1,
+                           w1s, rw, H, d.ks, d.S, c, g);
+  } else if (d.active) {
+    // rows past the tile's end reuse the first row; their results are dropped
+    const int r0 = d.row0 + (c < d.nrows ? c : 0), r1 = d.row0 + (16 + c < d.nrows ? 16 + c : 0);
+    int s0, s1;
+    if constexpr (ROUTES) {
+      s0 = __shfl(inv, r0, 64);
+      s1 = __shfl(inv, r1, 64);
+    } else {
+      s0 = r2s[r0];
+      s1 = TWO ? r2s[r1] : s0;
+    }
+    tile_dot<MX, U, TWO>(acc0, acc1, x + (int64_t)(s0 / K) * H, x + (int64_t)(s1 / K) * H, 0, w1, w1s, rw, H,
+                         d.u_begin, d.u_end, g);
+  }
+  split_reduce<TWO>(acc0, acc1, reinterpret_cast<float*>(smem), d.staged, d.S, d.ks, wave, lane);
+  if (d.ks == 0 && d.active) {
+    const int n = d.cg * 8 + (c & 7);
+#pragma unroll
+    for (int h = 0; h < (TWO ? 2 : 1); ++h) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * h + g * 4 + i;
+        const float gate = h ? acc1[i] : acc0[i];
+        const float up = __shfl_xor(gate, 8, 64);  // lane c ^ 8: the up value of the same column
+        if (c < 8 && m < d.nrows) act[(int64_t)(d.row0 + m) * F + n] = f32_to_bf16_bits(silu_f32(gate) * up);
+      }
+    }
+  }
+}
+
+// GEMM2 of one decode item.
+template <bool MX, bool TWO, typename YT>
+__device__ __forceinline__ void ffn2_item(const DecItem& d, const uint16_t* __restrict__ act, int H, int F,
+                                          const void* __restrict__ w2, const uint8_t* __restrict__ w2s,
+                                          YT* __restrict__ y, uint8_t* __restrict__ smem) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  const int64_t rw = (int64_t)d.e * H + d.cg * 16 + c;
+  f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+  if (d.staged) {
+    staged_dot<MX, kDecUnroll, TWO>(acc0, acc1, smem, d.nrows, d.active,
+                                    [&](int r) { return act + (int64_t)(d.row0 + r) * F; }, w2, w2s, rw, F, d.ks,
+                                    d.S, c, g);
+  } else if (d.active) {
+    // rows past the tile's end reuse the first row; their results are dropped
+    const uint16_t* a0 = act + (int64_t)(d.row0 + (c < d.nrows ? c : 0)) * F;
+    const uint16_t* a1 = act + (int64_t)(d.row0 + (16 + c < d.nrows ? 16 + c : 0)) * F;
+    tile_dot<MX, kDecUnroll, TWO>(acc0, acc1, a0, a1, 0, w2, w2s, rw, F, d.u_begin, d.u_end, g);
+  }
+  split_reduce<TWO>(acc0, acc1, reinterpret_cast<float*>(smem), d.staged, d.S, d.ks, wave, lane);
+  if (d.ks == 0 && d.active) {
+    const int n = d.cg * 16 + c;
+#pragma unroll
+    for (int h = 0; h < (TWO ? 2 : 1); ++h) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * h + g * 4 + i;
+        const float v = h ? acc1[i] : acc0[i];
+        if (m < d.nrows) {
+          if constexpr (sizeof(YT) == 2) y[(int64_t)(d.row0 + m) * H + n] = f32_to_bf16_bits(v);
+          else y[(int64_t)(d.row0 + m) * H + n] = v;
+        }
+      }
+    }
+  }
+}
+
 // GEMM1 + silu_and_mul for the decode regime.  Same operands as
 // ffn1_stream_kernel; with ROUTES, counts/offsets/r2s are unused and the
 // route table comes from `fr` (El <= 64, N <= 64).  A column group is 8 act
@@ -682,17 +878,15 @@ __global__ __launch_bounds__(kDecThreads) void ffn1_decode_kernel(
     const uint16_t* __restrict__ x, int K, int H, int F, int El, const void* __restrict__ w1,
     const uint8_t* __restrict__ w1s, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ r2s, uint16_t* __restrict__ act, FusedRoutes fr) {
-  constexpr int U = dec_unroll1<MX>();
-  __shared__ float red[kDecWaves][4][64];
-  __shared__ __attribute__((aligned(16))) uint8_t xs[MX ? kXsBytes : 16];
-  __shared__ int xtok[16];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[MX ? kXsBytes : kRedBytes];  // staged rows / partials
+  __shared__ int xtok[kDecBM];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const bool small = ROUTES || El <= 64;  // uniform
   TileTab tab{};
   int inv = -1;  // ROUTES: slot of row `lane`
   if constexpr (ROUTES) {
     const WaveRoutes wr = wave_routes(fr.ids, fr.N, fr.emap, fr.Eg, El);
-    tab = make_tile_tab(wr.cnt, wr.off, 16);
+    tab = make_tile_tab(wr.cnt, wr.off, kDecBM);
     inv = wr.inv;
     if (blockIdx.x == 0 && wave == 0) {
       if (lane < El) {
@@ -706,72 +900,30 @@ __global__ __launch_bounds__(kDecThreads) void ffn1_decode_kernel(
       }
     }
   } else if (small) {
-    tab = load_tile_tab(counts, offsets, El, 16);
+    tab = load_tile_tab(counts, offsets, El, kDecBM);
   }
-  const int tiles = small ? tab.total : count_tiles(counts, El, 16);
+  const int tiles = small ? tab.total : count_tiles(counts, El, kDecBM);
   const int CG = F / 8, units = H / 32;  // column groups of 8 act columns
-  const int S = decode_split(tiles, CG, units, gridDim.x, MX ? kSplitLatencyUnitsMX : kSplitLatencyUnits);
-  const int cpb = kDecWaves / S;         // column groups per item
+  DecItem d;
+  d.S = decode_split(tiles, CG, units, gridDim.x, MX ? kSplitLatencyUnitsMX : kSplitLatencyUnits);
+  const int cpb = kDecWaves / d.S;       // column groups per item
   const int ipt = (CG + cpb - 1) / cpb;  // items per tile
   const int items = tiles * ipt;
-  const int ks = wave % S, cgl = wave / S;
-  const int per = (units + S - 1) / S;
-  const int u_begin = min(units, ks * per), u_end = min(units, u_begin + per);
-  const bool stage_ok = MX && H <= kXsMaxK;  // uniform
+  d.ks = wave % d.S;
+  const int cgl = wave / d.S;
+  const int per = (units + d.S - 1) / d.S;
+  d.u_begin = min(units, d.ks * per);
+  d.u_end = min(units, d.u_begin + per);
 
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
     const int tile = it / ipt, cb = it % ipt;
-    int e = 0, row0 = 0, nrows = 0;
-    if (small) tab_find(tab, 16, tile, e, row0, nrows);
-    else find_tile(counts, offsets, El, 16, tile, e, row0, nrows);
-    const int cg = cb * cpb + cgl;
-    const bool active = cg < CG;
-    // W1 row of this lane's MFMA column: gate row (c < 8) or up row
-    const int64_t rw = (int64_t)e * 2 * F + (c >> 3) * F + cg * 8 + (c & 7);
-    f32x4 acc = {0, 0, 0, 0};
-    if (stage_ok && stage_item(S, nrows)) {  // uniform: one tile per item
-      const int n = nrows < 16 ? nrows : 16;
-      if (wave == 0) {  // the x row (token) of each of the item's rows
-        const int r = row0 + (lane < n ? lane : 0);
-        int slot;
-        if constexpr (ROUTES) slot = __shfl(inv, r, 64);
-        else slot = r2s[r];
-        if (lane < 16) xtok[lane] = slot / K;
-      }
-      lds_barrier();  // xtok visible; every wave is done with the previous item's rows
-      stage_rows(xs, n, H, [&](int r) { return x + (int64_t)xtok[r] * H; });
-      if (active)
-        acc = tile_dot<MX, U>(reinterpret_cast<const uint16_t*>(xs + (c < n ? c : 0) * (2 * H + kXsPad)), w1, w1s,
-                              rw, H, u_begin, u_end, g);
-    } else if (active) {
-      // rows past the tile's end reuse the first row; their results are dropped
-      const int r = row0 + (c < nrows ? c : 0);
-      int slot;
-      if constexpr (ROUTES) slot = __shfl(inv, r, 64);
-      else slot = r2s[r];
-      acc = tile_dot<MX, U>(x + (int64_t)(slot / K) * H, w1, w1s, rw, H, u_begin, u_end, g);
-    }
-    if (S > 1) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red[wave][i][lane] = acc[i];
-      __syncthreads();
-      if (ks == 0) {
-        for (int sp = 1; sp < S; ++sp) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i] += red[wave + sp][i][lane];
-        }
-      }
-      __syncthreads();  // red is rewritten by the next item
-    }
-    if (ks == 0 && active) {
-      const int n = cg * 8 + (c & 7);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = g * 4 + i;
-        const float up = __shfl_xor(acc[i], 8, 64);  // lane c ^ 8: the up value of the same column
-        if (c < 8 && m < nrows) act[(int64_t)(row0 + m) * F + n] = f32_to_bf16_bits(silu_f32(acc[i]) * up);
-      }
-    }
+    if (small) tab_find(tab, kDecBM, tile, d.e, d.row0, d.nrows);
+    else find_tile(counts, offsets, El, kDecBM, tile, d.e, d.row0, d.nrows);
+    d.cg = cb * cpb + cgl;
+    d.active = d.cg < CG;
+    d.staged = MX && stage_item(d.S, d.nrows);  // uniform: one tile per item
+    if (d.nrows > 16) ffn1_item<MX, ROUTES, true>(d, x, K, H, F, w1, w1s, r2s, inv, act, smem, xtok);
+    else ffn1_item<MX, ROUTES, false>(d, x, K, H, F, w1, w1s, r2s, inv, act, smem, xtok);
   }
 }
 
@@ -781,67 +933,33 @@ __global__ __launch_bounds__(kDecThreads) void ffn2_decode_kernel(
     const uint16_t* __restrict__ act, int H, int F, int El, const void* __restrict__ w2,
     const uint8_t* __restrict__ w2s, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     YT* __restrict__ y) {
-  __shared__ float red[kDecWaves][4][64];
-  __shared__ __attribute__((aligned(16))) uint8_t xs[MX ? kXsBytes : 16];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[MX ? kXsBytes : kRedBytes];  // staged rows / partials
+  const int wave = threadIdx.x >> 6;
   const bool small = El <= 64;  // uniform
   TileTab tab{};
-  if (small) tab = load_tile_tab(counts, offsets, El, 16);
-  const int tiles = small ? tab.total : count_tiles(counts, El, 16);
+  if (small) tab = load_tile_tab(counts, offsets, El, kDecBM);
+  const int tiles = small ? tab.total : count_tiles(counts, El, kDecBM);
   const int CG = H / 16, units = F / 32;
-  const int S = decode_split(tiles, CG, units, gridDim.x, MX ? kSplitLatencyUnitsMX : kSplitLatencyUnits);
-  const int cpb = kDecWaves / S;
+  DecItem d;
+  d.S = decode_split(tiles, CG, units, gridDim.x, MX ? kSplitLatencyUnitsMX : kSplitLatencyUnits);
+  const int cpb = kDecWaves / d.S;
   const int ipt = (CG + cpb - 1) / cpb;
   const int items = tiles * ipt;
-  const int ks = wave % S, cgl = wave / S;
-  const int per = (units + S - 1) / S;
-  const int u_begin = min(units, ks * per), u_end = min(units, u_begin + per);
-  const bool stage_ok = MX && F <= kXsMaxK;  // uniform
+  d.ks = wave % d.S;
+  const int cgl = wave / d.S;
+  const int per = (units + d.S - 1) / d.S;
+  d.u_begin = min(units, d.ks * per);
+  d.u_end = min(units, d.u_begin + per);
 
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
     const int tile = it / ipt, cb = it % ipt;
-    int e = 0, row0 = 0, nrows = 0;
-    if (small) tab_find(tab, 16, tile, e, row0, nrows);
-    else find_tile(counts, offsets, El, 16, tile, e, row0, nrows);
-    const int cg = cb * cpb + cgl;
-    const bool active = cg < CG;
-    const int64_t rw = (int64_t)e * H + cg * 16 + c;
-    f32x4 acc = {0, 0, 0, 0};
-    if (stage_ok && stage_item(S, nrows)) {  // uniform: one tile per item
-      const int n = nrows < 16 ? nrows : 16;
-      lds_barrier();  // every wave is done with the previous item's rows
-      stage_rows(xs, n, F, [&](int r) { return act + (int64_t)(row0 + r) * F; });
-      if (active)
-        acc = tile_dot<MX, kDecUnroll>(reinterpret_cast<const uint16_t*>(xs + (c < n ? c : 0) * (2 * F + kXsPad)), w2,
-                                       w2s, rw, F, u_begin, u_end, g);
-    } else if (active) {
-      // rows past the tile's end reuse the first row; their results are dropped
-      acc = tile_dot<MX, kDecUnroll>(act + (int64_t)(row0 + (c < nrows ? c : 0)) * F, w2, w2s, rw, F, u_begin, u_end,
-                                     g);
-    }
-    if (S > 1) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red[wave][i][lane] = acc[i];
-      __syncthreads();
-      if (ks == 0) {
-        for (int sp = 1; sp < S; ++sp) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i] += red[wave + sp][i][lane];
-        }
-      }
-      __syncthreads();
-    }
-    if (ks == 0 && active) {
-      const int n = cg * 16 + c;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = g * 4 + i;
-        if (m < nrows) {
-          if constexpr (sizeof(YT) == 2) y[(int64_t)(row0 + m) * H + n] = f32_to_bf16_bits(acc[i]);
-          else y[(int64_t)(row0 + m) * H + n] = acc[i];
-        }
-      }
-    }
+    if (small) tab_find(tab, kDecBM, tile, d.e, d.row0, d.nrows);
+    else find_tile(counts, offsets, El, kDecBM, tile, d.e, d.row0, d.nrows);
+    d.cg = cb * cpb + cgl;
+    d.active = d.cg < CG;
+    d.staged = MX && stage_item(d.S, d.nrows);  // uniform: one tile per item
+    if (d.nrows > 16) ffn2_item<MX, true>(d, act, H, F, w2, w2s, y, smem);
+    else ffn2_item<MX, false>(d, act, H, F, w2, w2s, y, smem);
   }
 }
 
@@ -1007,7 +1125,7 @@ __global__ __launch_bounds__(kDecThreads) void ffn2_combine_kernel(
         tab_find(tab, 16, tile, e, row0, nrows);
         const uint16_t* ar = act + (int64_t)(row0 + (c < nrows ? c : 0)) * F;
         const int64_t rw = (int64_t)e * H + cg * 16 + c;
-        finish_tile(tile_dot<MX, kDecUnroll>(ar, w2, w2s, rw, F, u_begin, u_end, g), row0, nrows);
+        finish_tile(tile_dot16<MX, kDecUnroll>(ar, w2, w2s, rw, F, u_begin, u_end, g), row0, nrows);
       }
     }
     for (int i = threadIdx.x; i < T * 16; i += kDecThreads) {

@@ -164,6 +164,42 @@ def test_decode_split_k_shapes(w_dtype, H, F, T, out_dtype):
     assert torch.equal(again["y"][:R], res["y"][:R]) and torch.equal(again["out"], res["out"])
 
 
+@pytest.mark.parametrize("w_dtype,H,F", [("mxfp4", 4096, 512), ("mxfp4", 4128, 96), ("mxfp4", 256, 2080),
+                                         ("mxfp4", 512, 384), ("bf16", 512, 384), ("bf16", 1120, 160),
+                                         ("bf16", 256, 2080)])
+@pytest.mark.parametrize("hot", [(40, 20), (32, 17)])
+def test_decode_tiles_past_16_rows(w_dtype, H, F, hot):
+    # Decode regime (fewer than 24 slots per local expert) with experts past
+    # 16 rows: one 32-row tile per expert up to 32 rows, both 16-row halves
+    # fed by each weight byte; 40 rows = a full 32-row tile and an 8-row one.
+    # MXFP4 A rows go through LDS in chunks of whole K units where 32 rows of
+    # the reduction do not fit (H = 4096, 4128 for GEMM1; F = 2080 for GEMM2,
+    # whose last chunk holds one unit).
+    T, K, Eg, El = 40, 4, 16, 8
+    rng = np.random.default_rng(H + F + hot[0])
+    emap = synth.random_expert_map(Eg, El, seed=H + F)
+    loc = np.flatnonzero(emap >= 0)
+    others = np.setdiff1d(np.arange(Eg), loc[:2])
+    rows = []
+    for t in range(T):  # distinct ids per row: the forced hot experts, then others
+        fixed = ([loc[0]] if t < hot[0] else []) + ([loc[1]] if t < hot[1] else [])
+        rest = rng.choice(others, size=K - len(fixed), replace=False)
+        rows.append(np.concatenate([np.array(fixed, dtype=np.int64), rest]))
+    ids = np.stack(rows)
+    ids = ids.astype(np.int32)
+    c0 = small_case(w_dtype, T, K, Eg, El, H, F, hot=False, seed=H + F + hot[1])
+    c = synth.MoECase(**{**c0.__dict__, "name": f"rows32_{w_dtype}_{H}_{F}_{hot}", "topk_ids": ids,
+                         "expert_map": emap})
+    ref = oracle.moe_layer(c)
+    counts = ref["counts"]
+    assert counts.max() == hot[0] and np.sort(counts)[-2] >= hot[1] and T * K / El < 24
+    res = run_layer(c)
+    compare_layer(c, res, ref, "rows32")
+    again = run_layer(c)
+    R = int(ref["offsets"][-1])
+    assert torch.equal(again["y"][:R], res["y"][:R]) and torch.equal(again["out"], res["out"])
+
+
 @pytest.mark.parametrize("pattern", ["same", "all_dup", "twelve_local"])
 def test_decode_deterministic(pattern, decode_weights_dev):
     c = synth.decode_case(pattern, "random", seed=5, with_weights=False)

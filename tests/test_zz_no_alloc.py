@@ -80,6 +80,6 @@ def test_noalloc_rejects_oversize():
     T = (64 << 20) // (c.K * c.F * 2) + 1
     x = torch.zeros((T, c.H), dtype=torch.bfloat16, device=d["x"].device)
     r2s_big = torch.full((T * c.K,), -1, dtype=torch.int32, device=x.device)
-    y = torch.empty((8, c.H), dtype=torch.bfloat16, device=x.device)
+    y = torch.empty((T * c.K, c.H), dtype=torch.bfloat16, device=x.device)  # sized as the call needs
     with pytest.raises(moe.MoeError, match="MOE_ERR_SCRATCH_LIMIT"):
         moe.moe_grouped_ffn_noalloc(x, c.K, d["w1"], d["w2"], counts, offsets, r2s_big, y=y)
