@@ -476,6 +476,8 @@ def bench_decode(dev, reps, only=None):
 
         t_a, t_b = ab_graph_ms(each(compact, ffn, combine), each(compact, ffn_control, combine), reps, dev)
         t_a, t_b = t_a / nvar, t_b / nvar
+        t_fa, t_fb = ab_graph_ms(each(ffn), each(ffn_control), reps, dev)
+        t_fa, t_fb = t_fa / nvar, t_fb / nvar
         # boundary fusion: compaction and combine inside the two FFN kernels,
         # A/B against the three separate calls (alternated replays)
         xws = torch.empty(moe.fused_experts_workspace_bytes(T, K, H, F, El, moe.MOE_BF16), dtype=torch.uint8,
@@ -496,9 +498,12 @@ def bench_decode(dev, reps, only=None):
              "boundary_fusion": {"upper_bound_saved_ms_43_layers": round((t_layer - t_ffn) * 43, 4),
                                  "ab_layer_ms": {"separate": round(t_sep, 4), "fused": round(t_fus, 4)},
                                  "saved_ms_43_layers": round((t_sep - t_fus) * 43, 4)}}
+        d["ab_ffn_ms"] = {"compact": round(t_fa, 4), "generic_control": round(t_fb, 4)}
         if wbytes:
             gbs = wbytes / (t_ffn / 1e3) / 1e9
-            d.update({"ffn_weight_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+            d.update({"ffn_weight_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                      "ab_ffn_hbm_frac": {"compact": round(wbytes / (t_fa / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                                          "generic_control": round(wbytes / (t_fb / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}})
         res[pat] = d
         log(f"[bench] decode {pat}: " + json.dumps(d))
     if only is not None:
@@ -593,10 +598,18 @@ def bench_mxfp4(dev, reps, only=None):
             t_ffn = graph_ms(each(ffn), reps, dev) / nvar
             t_layer = graph_ms(each(compact, ffn, combine), reps, dev) / nvar
             wbytes = float(np.mean(n_exp)) * per_expert
+            # A/B of the two MXFP4 arithmetics (bf16 widening vs the block-scaled
+            # f8f6f4 matrix cores), alternated replays of the FFN; the mode is read
+            # when a call is captured
+            prev = moe.moe_get_mxfp4_mma()
+            ab = ab_graph_ms(lambda: (moe.moe_set_mxfp4_mma(moe.MOE_MXFP4_MMA_BF16), each(ffn)())[1],
+                             lambda: (moe.moe_set_mxfp4_mma(moe.MOE_MXFP4_MMA_F8F6F4), each(ffn)())[1], reps, dev)
+            moe.moe_set_mxfp4_mma(prev)
+            mma_ab = {"bf16_widen_ffn_ms": round(ab[0] / nvar, 4), "f8f6f4_ffn_ms": round(ab[1] / nvar, 4)}
             d = {"T": T, "routes": routes, "local_slots": int((loc >= 0).sum()),
                  "local_experts_mean": round(float(np.mean(n_exp)), 2), "layer_ms": round(t_layer, 4),
                  "ffn_ms": round(t_ffn, 4), "tokens_per_s": round(T / (t_layer / 1e3), 1),
-                 "weight_bytes_mean": int(wbytes)}
+                 "weight_bytes_mean": int(wbytes), "mxfp4_mma_ab": mma_ab}
             if N <= 64:  # the boundary-fused layer (compaction in GEMM1, combine in GEMM2)
                 xws = torch.empty(max(moe.fused_experts_workspace_bytes(T, K, H, F, El, moe.MOE_MXFP4), 16),
                                   dtype=torch.uint8, device=dev)

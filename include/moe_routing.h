@@ -62,6 +62,18 @@ typedef enum moe_dtype {
                         layout written by moe_pack_ffn_weights */
 } moe_dtype;
 
+/* Arithmetic of MXFP4 expert GEMMs in the few-rows-per-expert (decode)
+ * kernels; see moe_set_mxfp4_mma. */
+typedef enum moe_mxfp4_mma {
+  MOE_MXFP4_MMA_BF16 = 0,  /* codes widened to bf16 in registers (exact), bf16
+                              matrix cores; activations used as given */
+  MOE_MXFP4_MMA_F8F6F4 = 1 /* CDNA4 block-scaled matrix cores on the e2m1 codes
+                              and their e8m0 scales as stored; activations split
+                              per 32 elements into two e4m3 terms (hi + lo) with
+                              their own e8m0 scales, which carry them to about
+                              2^-9 of the block's largest magnitude */
+} moe_mxfp4_mma;
+
 /*
  * moe_topk_softmax -- fused softmax + top-k gate.
  * Source: page "Upstream Reference: Deep-Spark xllm + vllm", section "Call
@@ -375,6 +387,26 @@ int moe_combine(const void* y, int y_dtype, const float* topk_weights, const int
                 int64_t T, int32_t K, int32_t H, void* out, int out_dtype, void* stream);
 
 /* Human-readable name of a moe_status value (static string). */
+/*
+ * moe_set_mxfp4_mma / moe_get_mxfp4_mma -- which arithmetic the MXFP4 expert
+ * GEMMs take in the decode kernels (fewer than 24 routed slots per local
+ * expert: moe_grouped_ffn, moe_grouped_ffn_noalloc, and GEMM1 of
+ * moe_fused_experts); larger batches always widen to bf16.  Source: b70 lab
+ * note "MTP1 M2 compact scheduler closure", correctness paragraph (the routed
+ * MXFP4 expert GEMMs), run here on the matrix-core formats of the target.
+ *
+ *   mode   a moe_mxfp4_mma value
+ *
+ * Process-wide; read on the host when a call is launched, so calls already
+ * launched (or captured in a graph) keep the arithmetic they were launched
+ * with.  Setting it from one thread while another launches MXFP4 calls
+ * leaves which of the two those calls take unspecified.  Non-finite
+ * activations give NaN outputs under MOE_MXFP4_MMA_F8F6F4.  Default:
+ * MOE_MXFP4_MMA_BF16.  Errors: MOE_ERR_INVALID_ARG for another mode.
+ */
+moe_status moe_set_mxfp4_mma(int mode);
+int moe_get_mxfp4_mma(void);
+
 const char* moe_status_string(int status);
 
 /* The hipError_t of the most recent MOE_ERR_HIP on the calling thread (0 if none). */

@@ -13,15 +13,17 @@ from typing import Optional, Tuple
 import torch
 
 from . import _lib
-from ._lib import MOE_BF16, MOE_BF16_TILED, MOE_F32, MOE_MXFP4
+from ._lib import MOE_BF16, MOE_BF16_TILED, MOE_F32, MOE_MXFP4, MOE_MXFP4_MMA_BF16, MOE_MXFP4_MMA_F8F6F4
 
 _LIB = _lib.load()
 
 __all__ = [
     "moe_topk_softmax", "moe_topk_sigmoid", "moe_route_compact", "moe_route_align", "moe_grouped_ffn",
     "moe_grouped_ffn_noalloc", "moe_grouped_ffn_control", "moe_fused_experts", "moe_topk_compact", "moe_combine", "moe_pack_ffn_weights", "moe_layer",
-    "moe_probe_read", "moe_probe_copy", "moe_probe_mfma", "moe_probe_gate_loads",
-    "MOE_F32", "MOE_BF16", "MOE_MXFP4", "MOE_BF16_TILED", "MoeError", "library_path",
+    "moe_probe_read", "moe_probe_copy", "moe_probe_mfma", "moe_probe_gate_loads", "moe_set_mxfp4_mma",
+    "moe_get_mxfp4_mma", "mxfp4_mma",
+    "MOE_F32", "MOE_BF16", "MOE_MXFP4", "MOE_BF16_TILED", "MOE_MXFP4_MMA_BF16", "MOE_MXFP4_MMA_F8F6F4", "MoeError",
+    "library_path",
 ]
 
 
@@ -290,6 +292,33 @@ def moe_route_align(topk_ids: torch.Tensor, expert_map: Optional[torch.Tensor], 
 
 def grouped_ffn_workspace_bytes(T: int, K: int, H: int, F: int, E_local: int, w_dtype: int) -> int:
     return int(_LIB.moe_grouped_ffn_workspace_bytes(T, K, H, F, E_local, w_dtype))
+
+
+def moe_set_mxfp4_mma(mode: int) -> None:
+    """MOE_MXFP4_MMA_BF16 or MOE_MXFP4_MMA_F8F6F4: the arithmetic of MXFP4
+    expert GEMMs in the decode kernels, for calls launched from now on."""
+    _check(_LIB.moe_set_mxfp4_mma(int(mode)), "moe_set_mxfp4_mma")
+
+
+def moe_get_mxfp4_mma() -> int:
+    return int(_LIB.moe_get_mxfp4_mma())
+
+
+class mxfp4_mma:
+    """Context manager: `with mxfp4_mma(MOE_MXFP4_MMA_F8F6F4): ...` sets the
+    MXFP4 decode arithmetic and restores the previous one on exit."""
+
+    def __init__(self, mode: int):
+        self.mode = int(mode)
+
+    def __enter__(self):
+        self.prev = moe_get_mxfp4_mma()
+        moe_set_mxfp4_mma(self.mode)
+        return self
+
+    def __exit__(self, *exc):
+        moe_set_mxfp4_mma(self.prev)
+        return False
 
 
 def moe_pack_ffn_weights(w1: torch.Tensor, w2: torch.Tensor, w1_tiled: Optional[torch.Tensor] = None,

@@ -12,6 +12,7 @@ HEADER = os.path.join(os.path.dirname(PKG_DIR), "include", "moe_routing.h")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP, MOE_ERR_WORKSPACE, MOE_ERR_SCRATCH_LIMIT = range(6)
 MOE_F32, MOE_BF16, MOE_MXFP4, MOE_BF16_TILED = range(4)
+MOE_MXFP4_MMA_BF16, MOE_MXFP4_MMA_F8F6F4 = 0, 1
 
 _p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -45,6 +46,8 @@ SIGNATURES = {
     "moe_probe_copy": (_int, [_p, _p, _sz, _p]),
     "moe_probe_mfma": (_int, [_i64, _i32, _p, _p]),
     "moe_probe_gate_loads": (_int, [_p, _i64, _i32, _i32, _p, _p, _p, _p]),
+    "moe_set_mxfp4_mma": (_int, [_int]),
+    "moe_get_mxfp4_mma": (_int, []),
     "moe_status_string": (ctypes.c_char_p, [_int]),
     "moe_last_hip_error": (_int, []),
     "moe_version": (ctypes.c_char_p, []),

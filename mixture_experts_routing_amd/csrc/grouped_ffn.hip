@@ -24,6 +24,8 @@
 // gate column and its up column.  MXFP4 weights are widened to bf16 in
 // registers with v_cvt_scalef32_pk_bf16_fp4 (exact: every e2m1 value times a
 // power-of-two scale in range is a bf16 value).
+#include <atomic>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -350,84 +352,6 @@ __global__ __launch_bounds__(kThreads) void ffn2_stream_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Generic persistent scheduler, kept as the A/B control of the b70 lab note
-// "MTP1 M2 compact scheduler closure" (the generic path it measures against:
-// a persistent grouped GEMM that scans every local expert and takes work from
-// a global atomic counter, at a pinned 64-column N tile).  Work item i is
-// (local expert i / NT, N tile i % NT) for every local expert, routed or
-// not; a block claims items from *work until none are left and skips
-// experts without rows.  Results equal the other paths' within rounding (the
-// same sums per output, K walked in the same order).
-
-constexpr int kControlGrid = 256;  // persistent blocks: one per compute unit
-
-__global__ void zero_counters_kernel(int32_t* __restrict__ w) { w[threadIdx.x] = 0; }
-
-template <int KS, bool MX>
-__global__ __launch_bounds__(kThreads) void ffn1_control_kernel(
-    const uint16_t* __restrict__ x, int K, int H, int F, int El, const void* __restrict__ w1,
-    const uint8_t* __restrict__ w1s, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ r2s, uint16_t* __restrict__ act, int32_t* __restrict__ work) {
-  __shared__ int item;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int NT = F / 64, total = El * NT;
-  while (true) {
-    if (threadIdx.x == 0) item = atomicAdd(work, 1);
-    __syncthreads();
-    const int it = item;
-    __syncthreads();
-    if (it >= total) break;
-    const int e = it / NT, n0 = (it % NT) * 64 + wave * 16;
-    const int cnt = counts[e];
-    const int base = offsets[e];
-    for (int m0 = 0; m0 < cnt; m0 += 16)
-      gemm1_cols<1, KS, MX>(x, K, H, F, w1, w1s, r2s, act, e, base + m0, min(16, cnt - m0), n0, lane);
-  }
-}
-
-template <int KS, bool MX, typename YT>
-__global__ __launch_bounds__(kThreads) void ffn2_control_kernel(
-    const uint16_t* __restrict__ act, int H, int F, int El, const void* __restrict__ w2,
-    const uint8_t* __restrict__ w2s, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-    YT* __restrict__ y, int32_t* __restrict__ work) {
-  __shared__ int item;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int NT = H / 64, total = El * NT;
-  while (true) {
-    if (threadIdx.x == 0) item = atomicAdd(work, 1);
-    __syncthreads();
-    const int it = item;
-    __syncthreads();
-    if (it >= total) break;
-    const int e = it / NT, n0 = (it % NT) * 64 + wave * 16;
-    const int cnt = counts[e];
-    const int base = offsets[e];
-    for (int m0 = 0; m0 < cnt; m0 += 16)
-      gemm2_cols<1, KS, MX, YT>(act, H, F, w2, w2s, y, e, base + m0, min(16, cnt - m0), n0, lane);
-  }
-}
-
-template <int KS, bool MX>
-hipError_t launch_control_k(const uint16_t* x, int K, int H, int F, int El, const void* w1, const uint8_t* w1s,
-                            const void* w2, const uint8_t* w2s, const int32_t* counts, const int32_t* offsets,
-                            const int32_t* r2s, void* y, int y_dtype, uint16_t* act, int32_t* work,
-                            hipStream_t stream) {
-  hipLaunchKernelGGL(zero_counters_kernel, dim3(1), dim3(2), 0, stream, work);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((ffn1_control_kernel<KS, MX>), dim3(kControlGrid), dim3(kThreads), 0, stream, x, K, H, F, El, w1, w1s,
-                     counts, offsets, r2s, act, work);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (y_dtype == MOE_BF16)
-    hipLaunchKernelGGL((ffn2_control_kernel<KS, MX, uint16_t>), dim3(kControlGrid), dim3(kThreads), 0, stream, act, H, F,
-                       El, w2, w2s, counts, offsets, static_cast<uint16_t*>(y), work + 1);
-  else
-    hipLaunchKernelGGL((ffn2_control_kernel<KS, MX, float>), dim3(kControlGrid), dim3(kThreads), 0, stream, act, H, F, El,
-                       w2, w2s, counts, offsets, static_cast<float*>(y), work + 1);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
 // Few rows per expert (decode): 16-wave blocks with an in-block K split.
 //
 // With a handful of rows per expert the FFN is a weight stream.  One wave per
@@ -728,6 +652,187 @@ __device__ __forceinline__ void staged_dot(f32x4& acc0, f32x4& acc1, uint8_t* __
   }
 }
 
+// ---------------------------------------------------------------------------
+// MXFP4 on the CDNA4 block-scaled matrix cores (MOE_MXFP4_MMA_F8F6F4).
+//
+// v_mfma_scale_f32_16x16x128_f8f6f4 multiplies a 16 x 128 A block by a
+// 128 x 16 B block with an e8m0 scale for every 32 K elements of each A row
+// and each B column.  Operand layout (lane l: row or column l % 16, lane
+// group g = l / 16; established with one-wave runs on inputs of known
+// structure):
+//   B, e2m1: the 32 nibbles of dwords 0-3 (low nibble first) are K
+//     [32g, 32g + 32);
+//   A, e4m3: bytes 0-15 are K [16g, 16g + 16), bytes 16-31 are K
+//     [64 + 16g, 64 + 16g + 16);
+//   scale_a / scale_b (byte 0): K block [32g, 32g + 32) of the lane's row or
+//     column;
+//   C: element q of lane l is row 4 (l / 16) + q, column l % 16.
+// K block b of one MFMA is MXFP4 unit u + b, so a weight lane loads unit
+// u + g whole (16 code bytes) and its scale byte, exactly as stored.  The
+// activations (x for GEMM1, act for GEMM2) are bf16: every 32-element unit
+// is split into two e4m3 terms with e8m0 scales, v = 2^e (hi + 2^-4 lo), where
+// e is the least exponent with max|v| <= 448 * 2^e (no element rounds past
+// e4m3's largest finite value, 448), hi = RNE(v 2^-e) and
+// lo = RNE(16 (v 2^-e - hi)).  |v 2^-e - hi| is at most half a unit in the
+// last place of hi (<= 16), so lo stays in range, and the two MFMAs (hi at
+// scale 2^e, lo at 2^(e-4)) see v to about 2^-9 of the unit's largest
+// element.  The split is made once per item while the rows are staged in
+// LDS: per row the hi bytes, then the lo bytes (the 64 bytes per unit a bf16
+// row takes), and the two scale bytes per unit in a small array beside them.
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kSxsMax = kXsBytes / 64;  // staged (row, unit) pairs: n x nu <= kXsBytes / 64
+
+// Stage elements [e0, e0 + ne) of rows [0, n) as e4m3 hi / lo bytes (row r at
+// xs + r (2 ne + kXsPad): hi at [0, ne), lo at [ne, 2 ne)) and their scale
+// bytes (sxs[r * ne / 32 + unit]: hi exponent + 127 in the low byte, lo in
+// the high byte), then a barrier.  The four 16-byte pieces of a unit fall on
+// four adjacent lanes (ne / 8 pieces per row, a multiple of 4, and the block
+// a multiple of 4 threads), which exchange their largest magnitude.
+template <typename SrcRow>
+__device__ __forceinline__ void stage_rows_f4(uint8_t* __restrict__ xs, uint16_t* __restrict__ sxs, int n, int e0,
+                                              int ne, SrcRow src_row) {
+  const int ppr = ne / 8, nu = ne / 32;
+  const int RS = 2 * ne + kXsPad;
+  for (int p = threadIdx.x; p < n * ppr; p += kDecThreads) {
+    const int r = p / ppr, q = p - r * ppr;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(src_row(r) + e0 + 8 * q);
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(v[i] << 16);
+      f[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    m = fmaxf(m, __shfl_xor(m, 2, 64));
+    const uint32_t mb = __float_as_uint(m);
+    // floor(log2 m) - 8, plus one where m's significand exceeds 1.75 (448 = 1.75 * 2^8)
+    int e = (int)(mb >> 23) - 127 - 8 + ((mb & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+    e = max(e, -123);  // lo's exponent e - 4 stays a valid e8m0 (zero rows: any)
+    const float s = __uint_as_float((uint32_t)(127 - e) << 23);
+    uint32_t hw[2], lw[2];
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const float h0 = f[4 * w] * s, h1 = f[4 * w + 1] * s, h2 = f[4 * w + 2] * s, h3 = f[4 * w + 3] * s;
+      int ph = __builtin_amdgcn_cvt_pk_fp8_f32(h0, h1, 0, false);
+      ph = __builtin_amdgcn_cvt_pk_fp8_f32(h2, h3, ph, true);
+      const float d0 = (h0 - __builtin_amdgcn_cvt_f32_fp8(ph, 0)) * 16.0f;
+      const float d1 = (h1 - __builtin_amdgcn_cvt_f32_fp8(ph, 1)) * 16.0f;
+      const float d2 = (h2 - __builtin_amdgcn_cvt_f32_fp8(ph, 2)) * 16.0f;
+      const float d3 = (h3 - __builtin_amdgcn_cvt_f32_fp8(ph, 3)) * 16.0f;
+      int pl = __builtin_amdgcn_cvt_pk_fp8_f32(d0, d1, 0, false);
+      pl = __builtin_amdgcn_cvt_pk_fp8_f32(d2, d3, pl, true);
+      hw[w] = (uint32_t)ph;
+      lw[w] = (uint32_t)pl;
+    }
+    *reinterpret_cast<u32x2*>(xs + r * RS + 8 * q) = u32x2{hw[0], hw[1]};
+    *reinterpret_cast<u32x2*>(xs + r * RS + ne + 8 * q) = u32x2{lw[0], lw[1]};
+    if ((q & 3) == 0) sxs[r * nu + (q >> 2)] = (uint16_t)((e + 127) | ((e + 123) << 8));
+  }
+  lds_barrier();
+}
+
+// NB MFMA steps of 4 units from unit u (the last may hold fewer: units at or
+// past u_end carry zero codes).  xr0 / xr1: the staged hi bytes of this
+// lane's A rows (c and 16 + c), lo bytes lo_off further; sx0 / sx1 their
+// scale pairs; ub: the chunk's first unit.  The code loads of all NB steps
+// are issued before the first MFMA.
+template <int NB, bool TWO>
+__device__ __forceinline__ void f4_steps(f32x4& acc0, f32x4& acc1, const uint8_t* __restrict__ xr0,
+                                         const uint8_t* __restrict__ xr1, const uint16_t* __restrict__ sx0,
+                                         const uint16_t* __restrict__ sx1, int lo_off, const uint8_t* __restrict__ wrow,
+                                         const uint8_t* __restrict__ srow, int u, int u_end, int ub, int g) {
+  u32x4 cw[NB];
+  uint32_t sb[NB];
+#pragma unroll
+  for (int s = 0; s < NB; ++s) {
+    const int uw = u + 4 * s + g;
+    const int ul = min(uw, u_end - 1);
+    const u32x4 t = *reinterpret_cast<const u32x4*>(wrow + 16 * ul);
+    cw[s] = uw < u_end ? t : u32x4{0u, 0u, 0u, 0u};
+    sb[s] = srow[ul];
+  }
+#pragma unroll
+  for (int s = 0; s < NB; ++s) {
+    const int k0 = u + 4 * s - ub;                  // chunk unit of K block 0
+    const int nl = min(4, u_end - (u + 4 * s));     // units in this step
+    const int h = g >> 1;
+    // K blocks past the step's units meet zero codes: read any staged bytes
+    const int oa = 32 * (k0 + (h < nl ? h : 0)) + 16 * (g & 1);
+    const int ob = 32 * (k0 + (2 + h < nl ? 2 + h : 0)) + 16 * (g & 1);
+    const int us = k0 + (g < nl ? g : 0);
+    const i32x8 bw = {(int)cw[s].x, (int)cw[s].y, (int)cw[s].z, (int)cw[s].w, 0, 0, 0, 0};
+    {
+      const u32x4 a0 = *reinterpret_cast<const u32x4*>(xr0 + oa), a1 = *reinterpret_cast<const u32x4*>(xr0 + ob);
+      const u32x4 l0 = *reinterpret_cast<const u32x4*>(xr0 + lo_off + oa);
+      const u32x4 l1 = *reinterpret_cast<const u32x4*>(xr0 + lo_off + ob);
+      const uint32_t sv = sx0[us];
+      const i32x8 ah = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+      const i32x8 al = {(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w, (int)l1.x, (int)l1.y, (int)l1.z, (int)l1.w};
+      acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ah, bw, acc0, 0, 4, 0, (int)(sv & 0xFFu), 0, (int)sb[s]);
+      acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(al, bw, acc0, 0, 4, 0, (int)(sv >> 8), 0, (int)sb[s]);
+    }
+    if constexpr (TWO) {
+      const u32x4 a0 = *reinterpret_cast<const u32x4*>(xr1 + oa), a1 = *reinterpret_cast<const u32x4*>(xr1 + ob);
+      const u32x4 l0 = *reinterpret_cast<const u32x4*>(xr1 + lo_off + oa);
+      const u32x4 l1 = *reinterpret_cast<const u32x4*>(xr1 + lo_off + ob);
+      const uint32_t sv = sx1[us];
+      const i32x8 ah = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+      const i32x8 al = {(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w, (int)l1.x, (int)l1.y, (int)l1.z, (int)l1.w};
+      acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ah, bw, acc1, 0, 4, 0, (int)(sv & 0xFFu), 0, (int)sb[s]);
+      acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(al, bw, acc1, 0, 4, 0, (int)(sv >> 8), 0, (int)sb[s]);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the next step's LDS reads stay after these MFMAs
+  }
+}
+
+// One wave's share of a decode item over staged e4m3 rows: units [u, u_end).
+template <bool TWO>
+__device__ __forceinline__ void tile_dot_f4(f32x4& acc0, f32x4& acc1, const uint8_t* __restrict__ xr0,
+                                            const uint8_t* __restrict__ xr1, const uint16_t* __restrict__ sx0,
+                                            const uint16_t* __restrict__ sx1, int lo_off, int ub,
+                                            const void* __restrict__ w, const uint8_t* __restrict__ ws, int64_t rw,
+                                            int kdim, int u, int u_end, int g) {
+  const uint8_t* wrow = static_cast<const uint8_t*>(w) + rw * (kdim / 2);
+  const uint8_t* srow = ws + rw * (kdim / 32);
+  if constexpr (!TWO)
+    for (; u + 32 <= u_end; u += 32) f4_steps<8, TWO>(acc0, acc1, xr0, xr1, sx0, sx1, lo_off, wrow, srow, u, u_end, ub, g);
+  for (; u + 16 <= u_end; u += 16) f4_steps<4, TWO>(acc0, acc1, xr0, xr1, sx0, sx1, lo_off, wrow, srow, u, u_end, ub, g);
+  if (u + 8 <= u_end) {
+    f4_steps<2, TWO>(acc0, acc1, xr0, xr1, sx0, sx1, lo_off, wrow, srow, u, u_end, ub, g);
+    u += 8;
+  }
+  for (; u < u_end; u += 4) f4_steps<1, TWO>(acc0, acc1, xr0, xr1, sx0, sx1, lo_off, wrow, srow, u, u_end, ub, g);
+}
+
+// The F4 counterpart of staged_dot: rows split into e4m3 terms chunk by
+// chunk; every split's share of a chunk is a whole number of MFMA steps.
+template <bool TWO, typename SrcRow>
+__device__ __forceinline__ void staged_dot_f4(f32x4& acc0, f32x4& acc1, uint8_t* __restrict__ xs,
+                                              uint16_t* __restrict__ sxs, int n, bool active, SrcRow src_row,
+                                              const void* __restrict__ w, const uint8_t* __restrict__ ws, int64_t rw,
+                                              int kdim, int ks, int S, int c, int g) {
+  const int units = kdim / 32;
+  const int kc = stage_chunk_units(n, units);
+  for (int c0 = 0; c0 < units; c0 += kc) {
+    const int nu = min(kc, units - c0);
+    lds_barrier();  // every wave is done with the previous rows in xs
+    stage_rows_f4(xs, sxs, n, 32 * c0, 32 * nu, src_row);
+    if (active) {
+      const int pc = ((nu + S - 1) / S + 3) & ~3;
+      const int ub = c0 + min(nu, ks * pc), ue = c0 + min(nu, ks * pc + pc);
+      const int RS = 64 * nu + kXsPad;
+      const int r0 = c < n ? c : 0, r1 = 16 + c < n ? 16 + c : 0;
+      tile_dot_f4<TWO>(acc0, acc1, xs + r0 * RS, xs + r1 * RS, sxs + r0 * nu, sxs + r1 * nu, 32 * nu, c0, w, ws, rw,
+                       kdim, ub, ue, g);
+    }
+  }
+}
+
 // Sum of the S split partials of an item, in split order, into the waves of
 // split 0 (red: kRedBytes of LDS; it may alias the staged rows, so the
 // caller passes `staged` to wait for every wave's last read of them first).
@@ -778,11 +883,12 @@ struct FusedRoutes {
 
 // GEMM1 + silu_and_mul of one decode item (TWO: a tile of more than 16
 // rows).  inv (ROUTES): lane r holds the slot of grouped row r.
-template <bool MX, bool ROUTES, bool TWO>
+template <bool MX, bool ROUTES, bool TWO, bool F4>
 __device__ __forceinline__ void ffn1_item(const DecItem& d, const uint16_t* __restrict__ x, int K, int H, int F,
                                           const void* __restrict__ w1, const uint8_t* __restrict__ w1s,
                                           const int32_t* __restrict__ r2s, int inv, uint16_t* __restrict__ act,
-                                          uint8_t* __restrict__ smem, int* __restrict__ xtok) {
+                                          uint8_t* __restrict__ smem, uint16_t* __restrict__ sxs,
+                                          int* __restrict__ xtok) {
   constexpr int U = dec_unroll1<MX>();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
   // W1 row of this lane's MFMA column: gate row (c < 8) or up row
@@ -796,9 +902,10 @@ __device__ __forceinline__ void ffn1_item(const DecItem& d, const uint16_t* __re
       else slot = r2s[r];
       if (lane < kDecBM) xtok[lane] = slot / K;
     }
-    // staged_dot's first barrier makes xtok visible
-    staged_dot<MX, U, TWO>(acc0, acc1, smem, d.nrows, d.active, [&](int r) { return x + (int64_t)xtok[r] * H; }, w1,
-                           w1s, rw, H, d.ks, d.S, c, g);
+    // the staging's first barrier makes xtok visible
+    const auto xrow = [&](int r) { return x + (int64_t)xtok[r] * H; };
+    if constexpr (F4) staged_dot_f4<TWO>(acc0, acc1, smem, sxs, d.nrows, d.active, xrow, w1, w1s, rw, H, d.ks, d.S, c, g);
+    else staged_dot<MX, U, TWO>(acc0, acc1, smem, d.nrows, d.active, xrow, w1, w1s, rw, H, d.ks, d.S, c, g);
   } else if (d.active) {
     // rows past the tile's end reuse the first row; their results are dropped
     const int r0 = d.row0 + (c < d.nrows ? c : 0), r1 = d.row0 + (16 + c < d.nrows ? 16 + c : 0);
@@ -830,17 +937,17 @@ __device__ __forceinline__ void ffn1_item(const DecItem& d, const uint16_t* __re
 }
 
 // GEMM2 of one decode item.
-template <bool MX, bool TWO, typename YT>
+template <bool MX, bool TWO, bool F4, typename YT>
 __device__ __forceinline__ void ffn2_item(const DecItem& d, const uint16_t* __restrict__ act, int H, int F,
                                           const void* __restrict__ w2, const uint8_t* __restrict__ w2s,
-                                          YT* __restrict__ y, uint8_t* __restrict__ smem) {
+                                          YT* __restrict__ y, uint8_t* __restrict__ smem, uint16_t* __restrict__ sxs) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
   const int64_t rw = (int64_t)d.e * H + d.cg * 16 + c;
   f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
   if (d.staged) {
-    staged_dot<MX, kDecUnroll, TWO>(acc0, acc1, smem, d.nrows, d.active,
-                                    [&](int r) { return act + (int64_t)(d.row0 + r) * F; }, w2, w2s, rw, F, d.ks,
-                                    d.S, c, g);
+    const auto arow = [&](int r) { return act + (int64_t)(d.row0 + r) * F; };
+    if constexpr (F4) staged_dot_f4<TWO>(acc0, acc1, smem, sxs, d.nrows, d.active, arow, w2, w2s, rw, F, d.ks, d.S, c, g);
+    else staged_dot<MX, kDecUnroll, TWO>(acc0, acc1, smem, d.nrows, d.active, arow, w2, w2s, rw, F, d.ks, d.S, c, g);
   } else if (d.active) {
     // rows past the tile's end reuse the first row; their results are dropped
     const uint16_t* a0 = act + (int64_t)(d.row0 + (c < d.nrows ? c : 0)) * F;
@@ -873,13 +980,14 @@ __device__ __forceinline__ void ffn2_item(const DecItem& d, const uint16_t* __re
 // yields both halves and a lane exchange (c <-> c + 8) pairs them for
 // silu(gate) * up -- twice as many items as 16 gate + 16 up columns would
 // give, which keeps every compute unit streaming when few tiles exist.
-template <bool MX, bool ROUTES>
+template <bool MX, bool ROUTES, bool F4>
 __global__ __launch_bounds__(kDecThreads) void ffn1_decode_kernel(
     const uint16_t* __restrict__ x, int K, int H, int F, int El, const void* __restrict__ w1,
     const uint8_t* __restrict__ w1s, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ r2s, uint16_t* __restrict__ act, FusedRoutes fr) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[MX ? kXsBytes : kRedBytes];  // staged rows / partials
   __shared__ int xtok[kDecBM];
+  __shared__ uint16_t sxs[F4 ? kSxsMax : 1];  // F4: scale bytes of the staged rows
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const bool small = ROUTES || El <= 64;  // uniform
   TileTab tab{};
@@ -921,19 +1029,20 @@ __global__ __launch_bounds__(kDecThreads) void ffn1_decode_kernel(
     else find_tile(counts, offsets, El, kDecBM, tile, d.e, d.row0, d.nrows);
     d.cg = cb * cpb + cgl;
     d.active = d.cg < CG;
-    d.staged = MX && stage_item(d.S, d.nrows);  // uniform: one tile per item
-    if (d.nrows > 16) ffn1_item<MX, ROUTES, true>(d, x, K, H, F, w1, w1s, r2s, inv, act, smem, xtok);
-    else ffn1_item<MX, ROUTES, false>(d, x, K, H, F, w1, w1s, r2s, inv, act, smem, xtok);
+    d.staged = F4 || (MX && stage_item(d.S, d.nrows));  // uniform: one tile per item; F4 always stages
+    if (d.nrows > 16) ffn1_item<MX, ROUTES, true, F4>(d, x, K, H, F, w1, w1s, r2s, inv, act, smem, sxs, xtok);
+    else ffn1_item<MX, ROUTES, false, F4>(d, x, K, H, F, w1, w1s, r2s, inv, act, smem, sxs, xtok);
   }
 }
 
 // GEMM2 for the decode regime: y = W2[e] act over the grouped rows.
-template <bool MX, typename YT>
+template <bool MX, typename YT, bool F4>
 __global__ __launch_bounds__(kDecThreads) void ffn2_decode_kernel(
     const uint16_t* __restrict__ act, int H, int F, int El, const void* __restrict__ w2,
     const uint8_t* __restrict__ w2s, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     YT* __restrict__ y) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[MX ? kXsBytes : kRedBytes];  // staged rows / partials
+  __shared__ uint16_t sxs[F4 ? kSxsMax : 1];  // F4: scale bytes of the staged rows
   const int wave = threadIdx.x >> 6;
   const bool small = El <= 64;  // uniform
   TileTab tab{};
@@ -957,26 +1066,140 @@ __global__ __launch_bounds__(kDecThreads) void ffn2_decode_kernel(
     else find_tile(counts, offsets, El, kDecBM, tile, d.e, d.row0, d.nrows);
     d.cg = cb * cpb + cgl;
     d.active = d.cg < CG;
-    d.staged = MX && stage_item(d.S, d.nrows);  // uniform: one tile per item
-    if (d.nrows > 16) ffn2_item<MX, true>(d, act, H, F, w2, w2s, y, smem);
-    else ffn2_item<MX, false>(d, act, H, F, w2, w2s, y, smem);
+    d.staged = F4 || (MX && stage_item(d.S, d.nrows));  // uniform: one tile per item; F4 always stages
+    if (d.nrows > 16) ffn2_item<MX, true, F4>(d, act, H, F, w2, w2s, y, smem, sxs);
+    else ffn2_item<MX, false, F4>(d, act, H, F, w2, w2s, y, smem, sxs);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Generic persistent scheduler, kept as the A/B control of the b70 lab note
+// "MTP1 M2 compact scheduler closure", timing paragraph (the generic path it
+// measures against: a persistent grouped GEMM that scans every local expert
+// and takes work from a global atomic counter, pinned to a 64-column N tile).
+// Only the scheduling differs from the decode kernels above: the blocks are
+// the same 16-wave blocks running the same item body (ffn1_item / ffn2_item:
+// staging, K split, 32-row tiles, epilogue), but work item i is (local expert
+// i / NT, 64-column N tile i % NT) for every local expert, routed or not,
+// claimed from a global counter until none are left; an item walks its
+// expert's rows tile by tile (none for an expert without rows).  The N tile
+// fixes the split: 64 act columns are 8 GEMM1 column groups (S = 2), 64
+// output columns 4 GEMM2 column groups (S = 4).  Results equal the decode
+// kernels' within rounding (same tiles; the split may differ).
+
+constexpr int kControlGrid = 256;  // persistent blocks: one per compute unit
+constexpr int kControlCols = 64;   // the pinned N tile
+
+__global__ void zero_counters_kernel(int32_t* __restrict__ w) { w[threadIdx.x] = 0; }
+
+// One claim from *work, broadcast to the block (uniform).
+__device__ __forceinline__ int claim_item(int32_t* __restrict__ work, int* __restrict__ slot) {
+  if (threadIdx.x == 0) *slot = atomicAdd(work, 1);
+  __syncthreads();
+  const int it = *slot;
+  __syncthreads();  // the slot is rewritten by the next claim
+  return it;
+}
+
+template <bool MX>
+__global__ __launch_bounds__(kDecThreads) void ffn1_control_kernel(
+    const uint16_t* __restrict__ x, int K, int H, int F, int El, const void* __restrict__ w1,
+    const uint8_t* __restrict__ w1s, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ r2s, uint16_t* __restrict__ act, int32_t* __restrict__ work) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[MX ? kXsBytes : kRedBytes];
+  __shared__ int xtok[kDecBM];
+  __shared__ int slot;
+  const int wave = threadIdx.x >> 6;
+  constexpr int cpb = kControlCols / 8;  // GEMM1 column groups per N tile
+  const int CG = F / 8, units = H / 32, NT = F / kControlCols, total = El * NT;
+  DecItem d;
+  d.S = kDecWaves / cpb;
+  d.ks = wave % d.S;
+  const int cgl = wave / d.S;
+  const int per = (units + d.S - 1) / d.S;
+  d.u_begin = min(units, d.ks * per);
+  d.u_end = min(units, d.u_begin + per);
+  for (int it = claim_item(work, &slot); it < total; it = claim_item(work, &slot)) {
+    d.e = it / NT;
+    d.cg = (it % NT) * cpb + cgl;
+    d.active = d.cg < CG;
+    const int cnt = counts[d.e], base = offsets[d.e];
+    for (int m0 = 0; m0 < cnt; m0 += kDecBM) {
+      d.row0 = base + m0;
+      d.nrows = min(kDecBM, cnt - m0);
+      d.staged = MX && stage_item(d.S, d.nrows);
+      if (d.nrows > 16) ffn1_item<MX, false, true, false>(d, x, K, H, F, w1, w1s, r2s, -1, act, smem, nullptr, xtok);
+      else ffn1_item<MX, false, false, false>(d, x, K, H, F, w1, w1s, r2s, -1, act, smem, nullptr, xtok);
+    }
+  }
+}
+
+template <bool MX, typename YT>
+__global__ __launch_bounds__(kDecThreads) void ffn2_control_kernel(
+    const uint16_t* __restrict__ act, int H, int F, int El, const void* __restrict__ w2,
+    const uint8_t* __restrict__ w2s, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    YT* __restrict__ y, int32_t* __restrict__ work) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[MX ? kXsBytes : kRedBytes];
+  __shared__ int slot;
+  const int wave = threadIdx.x >> 6;
+  constexpr int cpb = kControlCols / 16;  // GEMM2 column groups per N tile
+  const int CG = H / 16, units = F / 32, NT = H / kControlCols, total = El * NT;
+  DecItem d;
+  d.S = kDecWaves / cpb;
+  d.ks = wave % d.S;
+  const int cgl = wave / d.S;
+  const int per = (units + d.S - 1) / d.S;
+  d.u_begin = min(units, d.ks * per);
+  d.u_end = min(units, d.u_begin + per);
+  for (int it = claim_item(work, &slot); it < total; it = claim_item(work, &slot)) {
+    d.e = it / NT;
+    d.cg = (it % NT) * cpb + cgl;
+    d.active = d.cg < CG;
+    const int cnt = counts[d.e], base = offsets[d.e];
+    for (int m0 = 0; m0 < cnt; m0 += kDecBM) {
+      d.row0 = base + m0;
+      d.nrows = min(kDecBM, cnt - m0);
+      d.staged = MX && stage_item(d.S, d.nrows);
+      if (d.nrows > 16) ffn2_item<MX, true, false>(d, act, H, F, w2, w2s, y, smem, nullptr);
+      else ffn2_item<MX, false, false>(d, act, H, F, w2, w2s, y, smem, nullptr);
+    }
   }
 }
 
 template <bool MX>
+hipError_t launch_control(const uint16_t* x, int K, int H, int F, int El, const void* w1, const uint8_t* w1s,
+                          const void* w2, const uint8_t* w2s, const int32_t* counts, const int32_t* offsets,
+                          const int32_t* r2s, void* y, int y_dtype, uint16_t* act, int32_t* work,
+                          hipStream_t stream) {
+  hipLaunchKernelGGL(zero_counters_kernel, dim3(1), dim3(2), 0, stream, work);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((ffn1_control_kernel<MX>), dim3(kControlGrid), dim3(kDecThreads), 0, stream, x, K, H, F, El, w1,
+                     w1s, counts, offsets, r2s, act, work);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (y_dtype == MOE_BF16)
+    hipLaunchKernelGGL((ffn2_control_kernel<MX, uint16_t>), dim3(kControlGrid), dim3(kDecThreads), 0, stream, act, H,
+                       F, El, w2, w2s, counts, offsets, static_cast<uint16_t*>(y), work + 1);
+  else
+    hipLaunchKernelGGL((ffn2_control_kernel<MX, float>), dim3(kControlGrid), dim3(kDecThreads), 0, stream, act, H, F,
+                       El, w2, w2s, counts, offsets, static_cast<float*>(y), work + 1);
+  return hipGetLastError();
+}
+
+template <bool MX, bool F4>
 hipError_t launch_decode(const uint16_t* x, int K, int H, int F, int El, const void* w1, const uint8_t* w1s,
                          const void* w2, const uint8_t* w2s, const int32_t* counts, const int32_t* offsets,
                          const int32_t* r2s, void* y, int y_dtype, uint16_t* act, hipStream_t stream) {
-  hipLaunchKernelGGL((ffn1_decode_kernel<MX, false>), dim3(kDecGrid), dim3(kDecThreads), 0, stream, x, K, H, F, El,
-                     w1, w1s, counts, offsets, r2s, act, FusedRoutes{});
+  hipLaunchKernelGGL((ffn1_decode_kernel<MX, false, F4>), dim3(kDecGrid), dim3(kDecThreads), 0, stream, x, K, H, F,
+                     El, w1, w1s, counts, offsets, r2s, act, FusedRoutes{});
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (y_dtype == MOE_BF16)
-    hipLaunchKernelGGL((ffn2_decode_kernel<MX, uint16_t>), dim3(kDecGrid), dim3(kDecThreads), 0, stream, act, H, F,
-                       El, w2, w2s, counts, offsets, static_cast<uint16_t*>(y));
+    hipLaunchKernelGGL((ffn2_decode_kernel<MX, uint16_t, F4>), dim3(kDecGrid), dim3(kDecThreads), 0, stream, act, H,
+                       F, El, w2, w2s, counts, offsets, static_cast<uint16_t*>(y));
   else
-    hipLaunchKernelGGL((ffn2_decode_kernel<MX, float>), dim3(kDecGrid), dim3(kDecThreads), 0, stream, act, H, F, El,
-                       w2, w2s, counts, offsets, static_cast<float*>(y));
+    hipLaunchKernelGGL((ffn2_decode_kernel<MX, float, F4>), dim3(kDecGrid), dim3(kDecThreads), 0, stream, act, H, F,
+                       El, w2, w2s, counts, offsets, static_cast<float*>(y));
   return hipGetLastError();
 }
 
@@ -1149,9 +1372,14 @@ hipError_t launch_fused_k(const uint16_t* x, int64_t T, int K, int H, int F, con
                           const uint8_t* w2s, int32_t* counts, int32_t* offsets, int32_t* s2r, int32_t* r2s,
                           void* out, int out_dtype, uint16_t* act, hipStream_t stream) {
   const FusedRoutes fr{ids, emap, (int)(T * K), Eg, counts, offsets, s2r, r2s};
-  hipLaunchKernelGGL((ffn1_decode_kernel<MX, true>), dim3(kDecGrid), dim3(kDecThreads), 0, stream, x, K, H, F, El,
-                     w1, w1s, static_cast<const int32_t*>(nullptr), static_cast<const int32_t*>(nullptr),
-                     static_cast<const int32_t*>(nullptr), act, fr);
+  if (MX && mxfp4_mma_mode() == MOE_MXFP4_MMA_F8F6F4)
+    hipLaunchKernelGGL((ffn1_decode_kernel<MX, true, MX>), dim3(kDecGrid), dim3(kDecThreads), 0, stream, x, K, H, F,
+                       El, w1, w1s, static_cast<const int32_t*>(nullptr), static_cast<const int32_t*>(nullptr),
+                       static_cast<const int32_t*>(nullptr), act, fr);
+  else
+    hipLaunchKernelGGL((ffn1_decode_kernel<MX, true, false>), dim3(kDecGrid), dim3(kDecThreads), 0, stream, x, K, H,
+                       F, El, w1, w1s, static_cast<const int32_t*>(nullptr), static_cast<const int32_t*>(nullptr),
+                       static_cast<const int32_t*>(nullptr), act, fr);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || T == 0) return err;  // T == 0: counts and offsets (zeros) are written
   const unsigned grid = (unsigned)min(kDecGrid, H / 16);
@@ -1261,10 +1489,21 @@ hipError_t dispatch_stream(const uint16_t* x, int64_t N, int K, int H, int F, in
   if (avg >= 48) MOE_FFN_CASE(4);
   if (avg >= 24) MOE_FFN_CASE(2);
 #undef MOE_FFN_CASE
-  return launch_decode<MX>(x, K, H, F, El, w1, w1s, w2, w2s, counts, offsets, r2s, y, y_dtype, act, stream);
+  if constexpr (MX) {
+    if (mxfp4_mma_mode() == MOE_MXFP4_MMA_F8F6F4)
+      return launch_decode<true, true>(x, K, H, F, El, w1, w1s, w2, w2s, counts, offsets, r2s, y, y_dtype, act, stream);
+  }
+  return launch_decode<MX, false>(x, K, H, F, El, w1, w1s, w2, w2s, counts, offsets, r2s, y, y_dtype, act, stream);
 }
 
 }  // namespace
+
+namespace {
+std::atomic<int> g_mxfp4_mma{MOE_MXFP4_MMA_BF16};
+}  // namespace
+
+int mxfp4_mma_mode() { return g_mxfp4_mma.load(std::memory_order_relaxed); }
+void set_mxfp4_mma_mode(int mode) { g_mxfp4_mma.store(mode, std::memory_order_relaxed); }
 
 size_t grouped_ffn_workspace_bytes(int64_t N, int H, int F, int El, int w_dtype) {
   (void)H;
@@ -1314,16 +1553,10 @@ hipError_t launch_grouped_ffn_control(const void* x, int64_t T, int K, int H, in
   int32_t* work = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) +
                                              (grouped_ffn_workspace_bytes(N, H, F, El, w_dtype) + 255) / 256 * 256);
   const uint16_t* xb = static_cast<const uint16_t*>(x);
-  const bool k128 = (H % 128 == 0) && (F % 128 == 0);
   if (w_dtype == MOE_MXFP4)
-    return k128 ? launch_control_k<128, true>(xb, K, H, F, El, w1, w1s, w2, w2s, counts, offsets, r2s, y, y_dtype, act,
-                                              work, stream)
-                : launch_control_k<32, true>(xb, K, H, F, El, w1, w1s, w2, w2s, counts, offsets, r2s, y, y_dtype, act,
-                                             work, stream);
-  return k128 ? launch_control_k<128, false>(xb, K, H, F, El, w1, nullptr, w2, nullptr, counts, offsets, r2s, y,
-                                             y_dtype, act, work, stream)
-              : launch_control_k<32, false>(xb, K, H, F, El, w1, nullptr, w2, nullptr, counts, offsets, r2s, y,
-                                            y_dtype, act, work, stream);
+    return launch_control<true>(xb, K, H, F, El, w1, w1s, w2, w2s, counts, offsets, r2s, y, y_dtype, act, work, stream);
+  return launch_control<false>(xb, K, H, F, El, w1, nullptr, w2, nullptr, counts, offsets, r2s, y, y_dtype, act, work,
+                               stream);
 }
 
 size_t grouped_ffn_control_workspace_bytes(int64_t N, int H, int F, int El, int w_dtype) {

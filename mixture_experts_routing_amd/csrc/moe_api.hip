@@ -23,6 +23,14 @@ extern "C" {
 
 const char* moe_version(void) { return "moe_routing 0.1 (gfx950)"; }
 
+moe_status moe_set_mxfp4_mma(int mode) {
+  if (mode != MOE_MXFP4_MMA_BF16 && mode != MOE_MXFP4_MMA_F8F6F4) return MOE_ERR_INVALID_ARG;
+  moe::set_mxfp4_mma_mode(mode);
+  return MOE_OK;
+}
+
+int moe_get_mxfp4_mma(void) { return moe::mxfp4_mma_mode(); }
+
 const char* moe_status_string(int s) {
   switch (s) {
     case MOE_OK: return "MOE_OK";

@@ -202,6 +202,9 @@ hipError_t launch_route_align(const int32_t* topk_ids, int64_t N, const int32_t*
                               int32_t* block_expert, int32_t* slot_to_row, void* workspace, hipStream_t stream);
 
 size_t grouped_ffn_workspace_bytes(int64_t N, int H, int F, int El, int w_dtype);
+// MXFP4 decode arithmetic (a moe_mxfp4_mma value), process-wide
+int mxfp4_mma_mode();
+void set_mxfp4_mma_mode(int mode);
 hipError_t launch_grouped_ffn(const void* x, int x_dtype, int64_t T, int K, int H, int F,
                               int E_local, const void* w1, const uint8_t* w1s, const void* w2,
                               const uint8_t* w2s, int w_dtype, const int32_t* counts,

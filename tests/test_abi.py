@@ -204,3 +204,13 @@ def test_binding_checks_dtypes_shapes_and_sizes():
         moe.moe_fused_experts(x, z((2, 6), i32), z((3, 6), f32), w1, w2)      # weights [T, K]
     with pytest.raises(moe.MoeError, match="shape"):
         moe.moe_pack_ffn_weights(z((3, 256, 64), bf16), z((3, 64, 96), bf16))
+
+
+def test_mxfp4_mma_mode(lib):
+    # host-side state only: no kernel launch
+    prev = lib.moe_get_mxfp4_mma()
+    assert lib.moe_set_mxfp4_mma(1) == 0 and lib.moe_get_mxfp4_mma() == 1
+    assert lib.moe_set_mxfp4_mma(0) == 0 and lib.moe_get_mxfp4_mma() == 0
+    assert lib.moe_set_mxfp4_mma(2) == 1 and lib.moe_set_mxfp4_mma(-1) == 1  # MOE_ERR_INVALID_ARG
+    assert lib.moe_get_mxfp4_mma() == 0
+    lib.moe_set_mxfp4_mma(prev)
