@@ -126,3 +126,22 @@ def test_mode_switch_restores():
     assert moe.moe_get_mxfp4_mma() == moe.MOE_MXFP4_MMA_BF16
     with pytest.raises(moe.MoeError):
         moe.moe_set_mxfp4_mma(7)
+
+
+@pytest.mark.parametrize("T", [1, 9])
+def test_scale_range_both_arithmetics(T):
+    # e8m0 scales far from 2^0 (2^-27 .. 2^23 for W1, 2^-37 .. 2^13 for W2,
+    # with some blocks at byte 0 = 2^-127), so the scale reaches the matrix
+    # cores (f8f6f4) or the widening (bf16) over a wide range; outputs stay
+    # finite and within the MXFP4 bound of the oracle in both arithmetics
+    H, F = 512, 256
+    c = small_case("mxfp4", T, 4, 12, 6, H, F, hot=True, seed=77 + T)  # a local expert in every row
+    rng = np.random.default_rng(5 + T)
+    w1s = rng.integers(100, 151, size=c.w1_scale.shape, dtype=np.uint8)
+    w2s = rng.integers(90, 141, size=c.w2_scale.shape, dtype=np.uint8)
+    w1s[rng.random(w1s.shape) < 0.05] = 0
+    w2s[rng.random(w2s.shape) < 0.05] = 0
+    c = synth.MoECase(**{**c.__dict__, "name": f"mx_scales_T{T}", "w1_scale": w1s, "w2_scale": w2s})
+    ey, eo = both_modes(c, "scales")
+    assert np.isfinite(ey) and np.isfinite(eo)
+    assert oracle.moe_layer(c)["offsets"][-1] > 0  # not an all-remote batch
