@@ -69,7 +69,7 @@ def parse():
                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exit")
     p.add_argument("--profile", default="", metavar="WHAT",
                    help="only run one secondary for a kernel trace and exit: 'peaks' (the read, copy and "
-                        "MFMA probes), 'gate' (the five gate "
+                        "MFMA probes), 'libgemm' (torch.bmm on the expert GEMM shapes), 'gate' (the five gate "
                         "configurations), 'decode:PATTERN' (one decode route pattern, every path) or "
                         "'mxfp4[:T<n>_<routes>]' (the MXFP4 weight-streaming cases)")
     return p.parse_args()
@@ -308,6 +308,52 @@ def traffic_for(name):
         return d.get("bytes_per_launch")
     except Exception:
         return None
+
+
+# ---------------------------------------------------------------------------
+# context: the vendor GEMM library on the prefill FFN's expert GEMMs
+
+
+def library_gemm_reference(dev, reps=30):
+    """torch.bmm (hipBLASLt / rocBLAS) on dense per-expert GEMMs of the
+    prefill workload's shapes: 128 experts x 256 rows (the mean), H=2048,
+    F=768, bf16 -- without the row gather, the silu_and_mul epilogue or the
+    ragged row counts the library's own FFN handles.  A reference point for
+    the FFN's matrix-core fraction, not a step of the layer."""
+    import statistics
+
+    import torch
+
+    E, M, H, F = 128, 256, 2048, 768
+    out = {}
+    g = torch.Generator(device=dev).manual_seed(0)
+    for name, (k, n) in {"gemm1": (H, 2 * F), "gemm2": (F, H)}.items():
+        a = torch.randn((E, M, k), device=dev, dtype=torch.bfloat16, generator=g)
+        b = torch.randn((E, k, n), device=dev, dtype=torch.bfloat16, generator=g).contiguous()
+        for _ in range(10):
+            torch.bmm(a, b)
+        torch.cuda.synchronize()
+        t_end = time.perf_counter() + SETTLE_REPLAY_S
+        while time.perf_counter() < t_end:
+            torch.bmm(a, b)
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            torch.bmm(a, b)
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = statistics.median(x.elapsed_time(y) for x, y in evs)
+        flops = 2.0 * E * M * k * n
+        out[name] = {"shape": [E, M, k, n], "ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
+                     "mfma_frac": round(flops / ms / 1e9 / BF16_PEAK_TFLOPS, 4)}
+    tot = out["gemm1"]["ms"] + out["gemm2"]["ms"]
+    fl = 2.0 * E * M * (H * 2 * F + F * H)
+    out["both"] = {"ms": round(tot, 4), "mfma_frac": round(fl / tot / 1e9 / BF16_PEAK_TFLOPS, 4)}
+    log("[bench] library bmm at the expert GEMM shapes: " + json.dumps(out))
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -712,6 +758,8 @@ def main():
     if args.profile:
         if args.profile == "peaks":
             res = measured_peaks(dev)
+        elif args.profile == "libgemm":
+            res = library_gemm_reference(dev)
         elif args.profile == "gate":
             res = [bench_gate(dev, E, 64) for E in (128, 160)]
             res += [bench_gate(dev, E, 64, "sigmoid") for E in (128, 160, 256)]
@@ -732,6 +780,9 @@ def main():
     roofline["frac_of_measured_peak"] = round(roofline["achieved"] / peaks["mfma_bf16_tflops"], 4)
     roofline["hbm"]["min_bytes_frac_of_measured_read"] = round(roofline["hbm"]["min_bytes_gbs"] / peaks["read_gbs"], 4)
     if not args.no_secondary:
+        # context for the FFN's matrix-core fraction: the vendor library on
+        # dense per-expert GEMMs of the same shapes (no gather, no epilogue)
+        secondary["library_gemm_reference"] = library_gemm_reference(dev)
         reps = 50 if args.quick else 400
         secondary["gate"] = [bench_gate(dev, E, reps) for E in (128, 160)]
         secondary["gate"] += [bench_gate(dev, E, reps, "sigmoid") for E in (128, 160, 256)]
