@@ -200,6 +200,34 @@ def test_decode_tiles_past_16_rows(w_dtype, H, F, hot):
     assert torch.equal(again["y"][:R], res["y"][:R]) and torch.equal(again["out"], res["out"])
 
 
+@pytest.mark.parametrize("w_dtype", ["bf16", "mxfp4"])
+def test_decode_many_experts_past_16_rows(w_dtype):
+    # more than 64 local experts: the decode kernels find tiles through a
+    # scan of counts instead of the one-wave expert table; a few experts hold
+    # 17-40 rows (32-row tiles, a second tile past 32)
+    T, K, Eg, El, H, F = 48, 4, 160, 96, 256, 160
+    rng = np.random.default_rng(96)
+    emap = synth.random_expert_map(Eg, El, seed=96)
+    loc = np.flatnonzero(emap >= 0)
+    hot = loc[[0, 50, 95]]
+    rows = []
+    for t in range(T):
+        fixed = [hot[0]] + ([hot[1]] if t < 20 else []) + ([hot[2]] if t % 2 == 0 else [])
+        pool = np.setdiff1d(np.arange(Eg), hot)
+        rows.append(np.concatenate([np.array(fixed), rng.choice(pool, size=K - len(fixed), replace=False)]))
+    c0 = small_case(w_dtype, T, K, Eg, El, H, F, hot=False, seed=96)
+    c = synth.MoECase(**{**c0.__dict__, "name": f"many_experts_{w_dtype}", "topk_ids": np.stack(rows).astype(np.int32),
+                         "expert_map": emap})
+    ref = oracle.moe_layer(c)
+    assert ref["counts"].max() == T and T * K / El < 24
+    res = run_layer(c)
+    compare_layer(c, res, ref, "many-experts")
+    if w_dtype == "mxfp4":
+        with moe.mxfp4_mma(moe.MOE_MXFP4_MMA_F8F6F4):
+            res4 = run_layer(c)
+        compare_layer(c, res4, ref, "many-experts f8f6f4")
+
+
 @pytest.mark.parametrize("pattern", ["same", "all_dup", "twelve_local"])
 def test_decode_deterministic(pattern, decode_weights_dev):
     c = synth.decode_case(pattern, "random", seed=5, with_weights=False)
