@@ -21,7 +21,9 @@ Besides the contract fields the line carries:
                 bf16 matrix-core peak (the bar this call is held to); the HBM
                 rate on its minimum bytes (weights + x) and on the bytes with
                 the act / y hand-over rides along, and both against the
-                measured peaks
+                measured peaks; library_bmm_same_shapes_frac is the vendor
+                library's batched GEMM on dense per-expert operands of the
+                same shapes (no gather, no epilogue), for scale
   measured_peaks  what this GPU achieves in the same run: a 2 GiB streaming
                 read, a 1 GiB copy and a bf16 MFMA loop (library probes)
   cpu_baseline  the fp64 CPU oracle on a bounded token sample of the same
@@ -30,9 +32,12 @@ Besides the contract fields the line carries:
   secondary     gate throughput (65536 rows, E=128 and 160, bf16) in Mrows/s
                 and %-of-HBM with rotating buffers larger than the 256 MB
                 last-level cache; decode layer (M=2, top-6, 40 local
-                experts) per route pattern with achieved weight-stream GB/s.
-                Both are short calls, timed from HIP-graph replays so that
-                host launch overhead is not counted.
+                experts) per route pattern with achieved weight-stream GB/s,
+                the scheduler A/B against the generic control and the boundary
+                fusion A/B; MXFP4 decode (T = 2, 16, 64) with the A/B of its
+                two arithmetics; the padded layout; the library GEMM
+                reference.  The short calls are timed from HIP-graph replays
+                so that host launch overhead is not counted.
 """
 from __future__ import annotations
 
@@ -783,6 +788,7 @@ def main():
         # context for the FFN's matrix-core fraction: the vendor library on
         # dense per-expert GEMMs of the same shapes (no gather, no epilogue)
         secondary["library_gemm_reference"] = library_gemm_reference(dev)
+        roofline["library_bmm_same_shapes_frac"] = secondary["library_gemm_reference"]["both"]["mfma_frac"]
         reps = 50 if args.quick else 400
         secondary["gate"] = [bench_gate(dev, E, reps) for E in (128, 160)]
         secondary["gate"] += [bench_gate(dev, E, reps, "sigmoid") for E in (128, 160, 256)]
