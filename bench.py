@@ -25,7 +25,10 @@ Besides the contract fields the line carries:
                 library's batched GEMM on dense per-expert operands of the
                 same shapes (no gather, no epilogue), for scale
   measured_peaks  what this GPU achieves in the same run: a 2 GiB streaming
-                read, a 1 GiB copy and a bf16 MFMA loop (library probes)
+                read, a 1 GiB copy and a bf16 MFMA loop (library probes), the
+                loop with loop-invariant operands and with operands that
+                change every round as real data does, each with the clock it
+                ran at (data-dependent power lowers the clock)
   cpu_baseline  the fp64 CPU oracle on a bounded token sample of the same
                 workload, on this host's cores
   breakdown     per-call milliseconds of the step
@@ -409,7 +412,10 @@ def measured_peaks(dev):
     2 GiB and a 1 GiB -> 1 GiB copy (both larger than the 256 MB last-level
     cache; HIP events around each call, median of 10), and a bf16 MFMA loop
     (4 independent 32x32x16 MFMAs per round on register operands, 8192 waves;
-    median of 10 calls of ~4 ms) at the clock the chip runs under that load."""
+    median of 10 calls of ~4 ms) twice: with loop-invariant operands, and with
+    operands that change every round as real data does (half their bits
+    flip), which draws more power, so the chip runs it at a lower clock.  The
+    loop's own shader-clock and reference-clock counters give that clock."""
     import statistics
 
     import torch
@@ -442,14 +448,22 @@ def measured_peaks(dev):
     del src, dst
     blocks, iters = 2048, 8000
     mo = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
-    t_mfma = timed(lambda: moe.moe_probe_mfma(iters, blocks, mo))
+    clk = torch.zeros(blocks * 4 * 2, dtype=torch.int64, device=dev)
     flops = blocks * 4 * iters * 4 * 32768
+    mfma = {}
+    for name, toggle in (("constant", False), ("toggling", True)):
+        t = timed(lambda: moe.moe_probe_mfma_clock(iters, blocks, toggle, mo, clk))
+        c = clk.view(-1, 2).double().sum(0).tolist()
+        mfma[name] = {"tflops": round(flops / (t / 1e3) / 1e12, 1), "clock_ghz": round(c[0] / c[1] * 0.1, 3)}
     return {"read_gbs": round((2 << 30) / (t_read / 1e3) / 1e9, 1),
             "copy_gbs": round(2 * (1 << 30) / (t_copy / 1e3) / 1e9, 1),
-            "mfma_bf16_tflops": round(flops / (t_mfma / 1e3) / 1e12, 1),
+            "mfma_bf16_tflops": mfma["constant"]["tflops"],
+            "mfma_bf16_tflops_toggling": mfma["toggling"]["tflops"],
+            "mfma_clock_ghz": {k: v["clock_ghz"] for k, v in mfma.items()},
             "spec": {"hbm_gbs": HBM_PEAK_GBS, "mfma_bf16_tflops": BF16_PEAK_TFLOPS},
             "probes": "moe_probe_read (2 GiB), moe_probe_copy (1 GiB -> 1 GiB, bytes read + written), "
-                      "moe_probe_mfma (2048 x 256 threads, 8000 rounds of 4 MFMAs)"}
+                      "moe_probe_mfma_clock (2048 x 256 threads, 8000 rounds of 4 MFMAs; loop-invariant and "
+                      "toggling operands; clock = s_memtime cycles / s_memrealtime ticks x 100 MHz)"}
 
 
 # ---------------------------------------------------------------------------
@@ -780,9 +794,13 @@ def main():
     secondary = {"prefill_gate_compaction": gate_fusion}
     peaks = measured_peaks(dev)
     log(f"[bench] measured peaks: read {peaks['read_gbs']} GB/s, copy {peaks['copy_gbs']} GB/s, "
-        f"bf16 MFMA loop {peaks['mfma_bf16_tflops']} TFLOP/s")
+        f"bf16 MFMA loop {peaks['mfma_bf16_tflops']} TFLOP/s (constant operands, "
+        f"{peaks['mfma_clock_ghz']['constant']} GHz), {peaks['mfma_bf16_tflops_toggling']} TFLOP/s (toggling "
+        f"operands, {peaks['mfma_clock_ghz']['toggling']} GHz)")
     roofline["measured_peak"] = peaks["mfma_bf16_tflops"]
     roofline["frac_of_measured_peak"] = round(roofline["achieved"] / peaks["mfma_bf16_tflops"], 4)
+    roofline["measured_peak_toggling"] = peaks["mfma_bf16_tflops_toggling"]
+    roofline["frac_of_measured_peak_toggling"] = round(roofline["achieved"] / peaks["mfma_bf16_tflops_toggling"], 4)
     roofline["hbm"]["min_bytes_frac_of_measured_read"] = round(roofline["hbm"]["min_bytes_gbs"] / peaks["read_gbs"], 4)
     if not args.no_secondary:
         # context for the FFN's matrix-core fraction: the vendor library on

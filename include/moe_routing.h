@@ -329,7 +329,18 @@ size_t moe_fused_experts_workspace_bytes(int64_t T, int32_t K, int32_t H, int32_
  *   non-temporal stores.  bytes % 16 == 0, both 16-byte aligned.
  * moe_probe_mfma: blocks x 256 threads; every wave issues iters rounds of
  *   four independent v_mfma_f32_32x32x16_bf16 on register operands
- *   (4 x 32768 flops per round); out[blocks*256] receives the sums.
+ *   (4 x 32768 flops per round); out[blocks*256] receives the sums.  The
+ *   operands are loop-invariant constants.
+ * moe_probe_mfma_clock: the same loop; toggle = 1 starts the operands from
+ *   hashed values in [0.5, 2) with random signs and flips the sign and the 7
+ *   mantissa bits of every element each round (half the operand bits change
+ *   from one MFMA to the next, as with real data), toggle = 0 keeps the
+ *   constants of moe_probe_mfma.  If clocks is not null it receives, per
+ *   wave w (blocks*4 waves), clocks[2w] = shader-clock cycles of the loop
+ *   (s_memtime) and clocks[2w+1] = 100 MHz reference-clock ticks
+ *   (s_memrealtime): their ratio x 100 MHz is the clock the loop ran at.
+ *   MOE_ERR_INVALID_ARG for iters < 1, blocks < 1, a null out or toggle
+ *   other than 0/1.
  * moe_probe_gate_loads: the memory traffic of moe_topk_softmax's bf16 kernel
  *   for E = 8V, V in {8, 12, 16, 20, 24}, K <= 8 (the same grid, per-lane
  *   loads of the row's logits and K stores of weight, id and token-expert
@@ -341,6 +352,7 @@ size_t moe_fused_experts_workspace_bytes(int64_t T, int32_t K, int32_t H, int32_
 int moe_probe_read(const void* src, size_t bytes, uint32_t* out, size_t out_words, void* stream);
 int moe_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
 int moe_probe_mfma(int64_t iters, int32_t blocks, float* out, void* stream);
+int moe_probe_mfma_clock(int64_t iters, int32_t blocks, int32_t toggle, float* out, uint64_t* clocks, void* stream);
 int moe_probe_gate_loads(const void* logits, int64_t T, int32_t E, int32_t K, float* topk_weights,
                          int32_t* topk_ids, int32_t* token_expert_indices, void* stream);
 

@@ -20,7 +20,7 @@ _LIB = _lib.load()
 __all__ = [
     "moe_topk_softmax", "moe_topk_sigmoid", "moe_route_compact", "moe_route_align", "moe_grouped_ffn",
     "moe_grouped_ffn_noalloc", "moe_grouped_ffn_control", "moe_fused_experts", "moe_topk_compact", "moe_combine", "moe_pack_ffn_weights", "moe_layer",
-    "moe_probe_read", "moe_probe_copy", "moe_probe_mfma", "moe_probe_gate_loads", "moe_set_mxfp4_mma",
+    "moe_probe_read", "moe_probe_copy", "moe_probe_mfma", "moe_probe_mfma_clock", "moe_probe_gate_loads", "moe_set_mxfp4_mma",
     "moe_get_mxfp4_mma", "mxfp4_mma",
     "MOE_F32", "MOE_BF16", "MOE_MXFP4", "MOE_BF16_TILED", "MOE_MXFP4_MMA_BF16", "MOE_MXFP4_MMA_F8F6F4", "MoeError",
     "library_path",
@@ -525,6 +525,19 @@ def moe_probe_mfma(iters: int, blocks: int, out: torch.Tensor, stream=None) -> N
     _req(out, "out", _F32, blocks * 256)
     dev = _dev(out)
     _check(_LIB.moe_probe_mfma(iters, blocks, _ptr(out), _stream(stream, dev)), "moe_probe_mfma")
+
+
+def moe_probe_mfma_clock(iters: int, blocks: int, toggle: bool, out: torch.Tensor,
+                         clocks: Optional[torch.Tensor] = None, stream=None) -> None:
+    """The MFMA loop of moe_probe_mfma; toggle: operands change every round as
+    real data does.  clocks: int64 [blocks*4*2] (per wave: shader cycles, then
+    100 MHz ticks of the loop) or None."""
+    _req(out, "out", _F32, blocks * 256)
+    if clocks is not None:
+        _req(clocks, "clocks", torch.int64, blocks * 4 * 2)
+    dev = _dev(out, clocks)
+    _check(_LIB.moe_probe_mfma_clock(iters, blocks, 1 if toggle else 0, _ptr(out), _ptr(clocks), _stream(stream, dev)),
+           "moe_probe_mfma_clock")
 
 
 def moe_probe_gate_loads(logits: torch.Tensor, K: int, topk_weights: torch.Tensor, topk_ids: torch.Tensor,

@@ -45,6 +45,7 @@ SIGNATURES = {
     "moe_probe_read": (_int, [_p, _sz, _p, _sz, _p]),
     "moe_probe_copy": (_int, [_p, _p, _sz, _p]),
     "moe_probe_mfma": (_int, [_i64, _i32, _p, _p]),
+    "moe_probe_mfma_clock": (_int, [_i64, _i32, _i32, _p, _p, _p]),
     "moe_probe_gate_loads": (_int, [_p, _i64, _i32, _i32, _p, _p, _p, _p]),
     "moe_set_mxfp4_mma": (_int, [_int]),
     "moe_get_mxfp4_mma": (_int, []),

@@ -235,7 +235,11 @@ __device__ __forceinline__ void tile_kloop(const Tile& cur, const Tile& nxt, __a
   // The fragments of the step's first K half are requested first; its MFMAs
   // then alternate with the reads of the second half (one read after each
   // MFMA), so the first MFMAs do not queue behind the whole step's LDS reads.
-  auto compute = [&](int slot) {
+  // mid() runs between the two halves' MFMAs: the step's loads are issued
+  // there, while the MFMA unit still works through both waves' first halves,
+  // instead of after the step, where the two waves of a SIMD would issue them
+  // with nothing left in the MFMA pipe.
+  auto compute = [&](int slot, auto&& mid) {
     const uint8_t* base = lds + slot * STAGE;
     bf16x8 a[2][LIVE > 0 ? LIVE : 1], b[2][2];
 #pragma unroll
@@ -260,6 +264,8 @@ __device__ __forceinline__ void tile_kloop(const Tile& cur, const Tile& nxt, __a
     }
     if constexpr (LIVE > 2) __builtin_amdgcn_sched_group_barrier(0x008, LIVE - 2, 0);
     __builtin_amdgcn_sched_barrier(0);
+    mid();
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int mb = 0; mb < LIVE; ++mb) {
       acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[1][0], a[1][mb], acc[mb][0], 0, 0, 0);
@@ -273,13 +279,14 @@ __device__ __forceinline__ void tile_kloop(const Tile& cur, const Tile& nxt, __a
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    compute(g % kStages);
-    __builtin_amdgcn_sched_barrier(0);
     // the slot read in step g-1 is free: every wave has passed the barrier
     const int ahead = kt + kStages - 1;
     const int fill = (g + kStages - 1) % kStages;
-    if (ahead < KT) dma(fill, cur, ahead, true);
-    else dma(fill, nxt, ahead - KT, nxt.valid);
+    compute(g % kStages, [&] {
+      if (ahead < KT) dma(fill, cur, ahead, true);
+      else dma(fill, nxt, ahead - KT, nxt.valid);
+    });
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 

@@ -341,7 +341,14 @@ int moe_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
 
 int moe_probe_mfma(int64_t iters, int32_t blocks, float* out, void* stream) {
   if (iters < 1 || blocks < 1 || !out) return MOE_ERR_INVALID_ARG;
-  return hip_status(moe::launch_probe_mfma(iters, blocks, out, static_cast<hipStream_t>(stream)));
+  return hip_status(moe::launch_probe_mfma(iters, blocks, false, out, nullptr, static_cast<hipStream_t>(stream)));
+}
+
+int moe_probe_mfma_clock(int64_t iters, int32_t blocks, int32_t toggle, float* out, uint64_t* clocks, void* stream) {
+  if (iters < 1 || blocks < 1 || !out || (toggle != 0 && toggle != 1)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_probe_mfma(iters, blocks, toggle != 0, out,
+                                           reinterpret_cast<unsigned long long*>(clocks),
+                                           static_cast<hipStream_t>(stream)));
 }
 
 int moe_probe_gate_loads(const void* logits, int64_t T, int32_t E, int32_t K, float* topk_weights,

@@ -266,7 +266,8 @@ hipError_t launch_combine(const void* y, int y_dtype, const float* w, const int3
 // measurement probes (no step of the layer)
 hipError_t launch_probe_read(const void* src, int64_t bytes, uint32_t* out, hipStream_t stream);
 hipError_t launch_probe_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
-hipError_t launch_probe_mfma(int64_t iters, int blocks, float* out, hipStream_t stream);
+hipError_t launch_probe_mfma(int64_t iters, int blocks, bool toggle, float* out, unsigned long long* clk,
+                             hipStream_t stream);
 hipError_t launch_probe_gate_loads(const uint16_t* logits, int64_t T, int E, int K, float* w, int32_t* ids,
                                    int32_t* tei, hipStream_t stream);
 int probe_read_out_words();

@@ -52,26 +52,56 @@ __global__ __launch_bounds__(kProbeThreads) void probe_copy_kernel(const u32x4* 
 
 // bf16 matrix-core loop: every wave issues iters rounds of four independent
 // v_mfma_f32_32x32x16_bf16 (4 x 32768 flops per round) on register operands;
-// the accumulators are summed into out[thread].
-__global__ __launch_bounds__(kProbeThreads) void probe_mfma_kernel(int64_t iters, float* __restrict__ out) {
+// the accumulators are summed into out[thread].  TOGGLE: the operands start
+// from hashed bf16 values in [0.5, 2) with random signs, and every round
+// flips the sign and the 7 mantissa bits of each element (so half the
+// operand bits change from one MFMA to the next, as with real data; the
+// exponents stay, so every value stays finite); otherwise the operands are
+// loop-invariant small constants.  clk (if not null) receives per wave the
+// shader-clock cycles (s_memtime) and the 100 MHz reference-clock ticks
+// (s_memrealtime) the loop took: clk[2w], clk[2w+1].
+template <bool TOGGLE>
+__global__ __launch_bounds__(kProbeThreads) void probe_mfma_kernel(int64_t iters, float* __restrict__ out,
+                                                                   unsigned long long* __restrict__ clk) {
   const int lane = threadIdx.x & 63;
-  bf16x8 a, b;
+  const int64_t tid = (int64_t)blockIdx.x * kProbeThreads + threadIdx.x;
+  u32x4 ua, ub;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    a[i] = (__bf16)(0.001f * (float)((lane + i) & 7));
-    b[i] = (__bf16)(0.002f * (float)((lane * 3 + i) & 7));
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (TOGGLE) {
+      const uint32_t h = ((uint32_t)tid * 4u + (uint32_t)i) * 2654435761u;
+      const uint32_t h2 = h * 2246822519u + 3266489917u;
+      // two bf16 per word: exponent of 0.5 or 1 (0x3F00 | mantissa), sign from the hash
+      ua[i] = ((0x3F00u | ((h >> 17) & 0xFFu)) << 16 | (0x3F00u | ((h >> 9) & 0xFFu))) ^ (h & 0x80008000u);
+      ub[i] = ((0x3F00u | ((h2 >> 17) & 0xFFu)) << 16 | (0x3F00u | ((h2 >> 9) & 0xFFu))) ^ (h2 & 0x80008000u);
+    } else {
+      ua[i] = pack_bf16x2(0.001f * (float)((lane + 2 * i) & 7), 0.001f * (float)((lane + 2 * i + 1) & 7));
+      ub[i] = pack_bf16x2(0.002f * (float)((lane * 3 + 2 * i) & 7), 0.002f * (float)((lane * 3 + 2 * i + 1) & 7));
+    }
   }
   f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
   for (int64_t it = 0; it < iters; ++it) {
+    if constexpr (TOGGLE) {
+      ua ^= (u32x4){0x807F807Fu, 0x807F807Fu, 0x807F807Fu, 0x807F807Fu};
+      ub ^= (u32x4){0x807F807Fu, 0x807F807Fu, 0x807F807Fu, 0x807F807Fu};
+    }
+    const bf16x8 a = __builtin_bit_cast(bf16x8, ua), b = __builtin_bit_cast(bf16x8, ub);
     c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
     c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c1, 0, 0, 0);
     c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, c2, 0, 0, 0);
     c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, b, c3, 0, 0, 0);
   }
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
   float s = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
-  out[(int64_t)blockIdx.x * kProbeThreads + threadIdx.x] = s;
+  out[tid] = s;
+  if (clk && lane == 0) {
+    const int64_t w = tid >> 6;
+    clk[2 * w] = t1 - t0;
+    clk[2 * w + 1] = r1 - r0;
+  }
 }
 
 // The bf16 gate's memory traffic without its selection: the same grid (8
@@ -125,8 +155,12 @@ hipError_t launch_probe_copy(const void* src, void* dst, int64_t bytes, hipStrea
   return hipGetLastError();
 }
 
-hipError_t launch_probe_mfma(int64_t iters, int blocks, float* out, hipStream_t stream) {
-  hipLaunchKernelGGL(probe_mfma_kernel, dim3((unsigned)blocks), dim3(kProbeThreads), 0, stream, iters, out);
+hipError_t launch_probe_mfma(int64_t iters, int blocks, bool toggle, float* out, unsigned long long* clk,
+                             hipStream_t stream) {
+  if (toggle)
+    hipLaunchKernelGGL(probe_mfma_kernel<true>, dim3((unsigned)blocks), dim3(kProbeThreads), 0, stream, iters, out, clk);
+  else
+    hipLaunchKernelGGL(probe_mfma_kernel<false>, dim3((unsigned)blocks), dim3(kProbeThreads), 0, stream, iters, out, clk);
   return hipGetLastError();
 }
 

@@ -214,3 +214,16 @@ def test_mxfp4_mma_mode(lib):
     assert lib.moe_set_mxfp4_mma(2) == 1 and lib.moe_set_mxfp4_mma(-1) == 1  # MOE_ERR_INVALID_ARG
     assert lib.moe_get_mxfp4_mma() == 0
     lib.moe_set_mxfp4_mma(prev)
+
+
+@_no_gpu
+def test_probe_validation(lib):
+    f = lib.moe_probe_mfma_clock
+    assert f(0, 4, 0, FAKE, NULL, NULL) == 1       # iters < 1
+    assert f(10, 0, 0, FAKE, NULL, NULL) == 1      # blocks < 1
+    assert f(10, 4, 2, FAKE, NULL, NULL) == 1      # toggle not 0/1
+    assert f(10, 4, 1, NULL, NULL, NULL) == 1      # null out
+    assert lib.moe_probe_mfma(0, 4, FAKE, NULL) == 1
+    assert lib.moe_probe_read(FAKE, 24, FAKE, 4096 * 256, NULL) == 1      # bytes % 16
+    assert lib.moe_probe_read(FAKE, 32, FAKE, 100, NULL) == 4             # out too short
+    assert lib.moe_probe_copy(FAKE, FAKE, 8, NULL) == 1
