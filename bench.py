@@ -802,6 +802,13 @@ def main():
     roofline["measured_peak_toggling"] = peaks["mfma_bf16_tflops_toggling"]
     roofline["frac_of_measured_peak_toggling"] = round(roofline["achieved"] / peaks["mfma_bf16_tflops_toggling"], 4)
     roofline["hbm"]["min_bytes_frac_of_measured_read"] = round(roofline["hbm"]["min_bytes_gbs"] / peaks["read_gbs"], 4)
+    if roofline["traffic"]:
+        # the bytes the counters saw (reads and writes) at the call's duration,
+        # against the measured streaming-read and copy rates of the same run
+        tg = roofline["traffic"] / (roofline["avg_launch_ms"] / 1e3) / 1e9
+        roofline["hbm"]["traffic_gbs"] = round(tg, 1)
+        roofline["hbm"]["traffic_frac_of_measured_read"] = round(tg / peaks["read_gbs"], 4)
+        roofline["hbm"]["traffic_frac_of_measured_copy"] = round(tg / peaks["copy_gbs"], 4)
     if not args.no_secondary:
         # context for the FFN's matrix-core fraction: the vendor library on
         # dense per-expert GEMMs of the same shapes (no gather, no epilogue)
