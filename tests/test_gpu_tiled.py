@@ -84,6 +84,46 @@ def test_tiled_layer_matches_rowmajor_and_oracle(name):
         assert torch.equal(til["out"], row["out"])
 
 
+def skewed_case(T, Eg, El, K, H, F, seed):
+    """A prefill layer whose router favours a few experts: local expert 0 takes
+    about every token (several 320-row M-tiles and a partial last one),
+    experts 1 and 2 many, the last four (almost surely) none; with
+    E_global > E_local some routes are remote."""
+    bias = np.zeros(Eg, np.float32)
+    bias[0], bias[1], bias[2] = 7.0, 3.5, 1.5
+    bias[El - 4:El] = -40.0
+    logits = synth.round_to_bf16_bits(synth.f32_normal((T, Eg), 2.0, seed, 91) + bias)
+    c = synth.prefill_layer(seed=seed, T=T, E=El, K=K, H=H, F=F)
+    c.name = f"skewed_T{T}_Eg{Eg}_El{El}_K{K}"
+    c.E_global = Eg
+    c.logits = logits
+    c.expert_map = synth.contiguous_expert_map(Eg, El, 0) if El < Eg else None
+    return c
+
+
+@pytest.mark.parametrize("T,Eg,El,K,H,F", [(2048, 16, 16, 4, 256, 128),    # 320-row tiles, up to 7 per expert
+                                           (1536, 24, 16, 6, 512, 256),    # and remote routes
+                                           (1024, 16, 16, 2, 256, 256)])   # 128-row tiles
+def test_tiled_skewed_routes(T, Eg, El, K, H, F):
+    c = skewed_case(T, Eg, El, K, H, F, seed=3)
+    d = case_to_device(c)
+    ref = oracle.moe_layer(c)
+    counts = np.diff(ref["offsets"])
+    R = int(ref["offsets"][-1])
+    print(f"[tiled] skewed T={T} Eg={Eg} El={El} K={K}: rows per expert {counts.tolist()}", flush=True)
+    assert counts.max() > 2 * 320 and (counts == 0).sum() >= 1  # the shapes this case is for
+    row = run(c, d, False)
+    t1, t2 = moe.moe_pack_ffn_weights(d["w1"], d["w2"])
+    d_t = dict(d)
+    d_t["w1"], d_t["w2"] = t1, t2
+    til = run(c, d_t, True)
+    ey = rel_max_err(host_f64(til["y"][:R]), ref["y"])
+    eo = rel_max_err(host_f64(til["out"]), ref["out"])
+    print(f"[tiled] skewed: y err {ey:.3e} out err {eo:.3e}", flush=True)
+    assert ey <= 1e-2 and eo <= 1e-2
+    assert torch.equal(til["y"][:R], row["y"][:R]) and torch.equal(til["out"], row["out"])
+
+
 def test_tiled_full_prefill_bit_equal_to_rowmajor():
     c = synth.prefill_layer(0)
     d = case_to_device(c)
