@@ -299,6 +299,15 @@ def bench_prefill(args, dev):
     return c, ms_per_step, per, roofline, settle, gate_fusion
 
 
+def traffic_parts_for(name):
+    """(read bytes, written bytes) per launch from the same counter runs as
+    traffic_for, or None under the same conditions."""
+    if traffic_for(name) is None:
+        return None
+    d = json.load(open(os.path.join(ROOT, "profiles", f"traffic_{name}.json")))
+    return (d["fetch_kib_per_launch"] * 1024 * d["fetch_scale"], d["write_kib_per_launch"] * 1024 * d["write_scale"])
+
+
 def traffic_for(name):
     """HBM bytes per launch from the committed rocprofv3 counter runs
     (FETCH_SIZE and WRITE_SIZE scaled by a plain-copy calibration), if they
@@ -809,6 +818,17 @@ def main():
         roofline["hbm"]["traffic_gbs"] = round(tg, 1)
         roofline["hbm"]["traffic_frac_of_measured_read"] = round(tg / peaks["read_gbs"], 4)
         roofline["hbm"]["traffic_frac_of_measured_copy"] = round(tg / peaks["copy_gbs"], 4)
+        parts = traffic_parts_for("grouped_ffn_prefill")
+        if parts:
+            # reads at the streaming-read rate, writes at the rate the copy
+            # (half reads, half writes) leaves for them: the time this traffic
+            # needs at the rates this box reaches
+            rd, wr = parts
+            read_s = 1.0 / (peaks["read_gbs"] * 1e9)
+            write_s = max(2.0 / (peaks["copy_gbs"] * 1e9) - read_s, read_s)
+            floor_ms = (rd * read_s + wr * write_s) * 1e3
+            roofline["hbm"]["traffic_floor_ms"] = round(floor_ms, 4)
+            roofline["hbm"]["traffic_floor_frac"] = round(floor_ms / roofline["avg_launch_ms"], 4)
     if not args.no_secondary:
         # context for the FFN's matrix-core fraction: the vendor library on
         # dense per-expert GEMMs of the same shapes (no gather, no epilogue)
