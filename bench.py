@@ -822,7 +822,7 @@ def main():
         if parts:
             # reads at the streaming-read rate, writes at the rate the copy
             # (half reads, half writes) leaves for them: the time this traffic
-            # needs at the rates this box reaches
+            # needs at the rates this GPU reaches
             rd, wr = parts
             read_s = 1.0 / (peaks["read_gbs"] * 1e9)
             write_s = max(2.0 / (peaks["copy_gbs"] * 1e9) - read_s, read_s)
