@@ -56,6 +56,26 @@ def test_tiny_layer_f32():
     assert ey < 1e-5 and eo < 1e-5
 
 
+@pytest.mark.parametrize("T,Eg,El,K,H,F,renorm", [(37, 12, 8, 3, 96, 40, False),   # odd sizes, remote routes
+                                                    (200, 8, 8, 4, 64, 128, True),     # renormalised, all local
+                                                    (1, 5, 3, 5, 32, 16, True)])       # one token, every expert
+def test_f32_layer_shapes(T, Eg, El, K, H, F, renorm):
+    """The fp32 path (every step in fp32) at shapes other than the tiny
+    layer's: fp32 end to end stays far inside the bound of the fp64 oracle."""
+    c = synth.tiny_layer(T)
+    c.name = f"f32_T{T}_Eg{Eg}_El{El}_K{K}_H{H}_F{F}"
+    c.T, c.E_global, c.E_local, c.K, c.H, c.F, c.renormalize = T, Eg, El, K, H, F, renorm
+    c.logits = synth.f32_normal((T, Eg), 1.0, T, 71)
+    c.x = synth.f32_normal((T, H), 1.0, T, 72)
+    c.w1 = synth.f32_normal((El, 2 * F, H), 0.05, T, 73)
+    c.w2 = synth.f32_normal((El, H, F), 0.05, T, 74)
+    c.expert_map = synth.random_expert_map(Eg, El, T) if El < Eg else None
+    res = run_layer(c)
+    ref = oracle.moe_layer(c)
+    ey, eo = compare_layer(c, res, ref, "f32 shapes")
+    assert ey < 1e-5 and eo < 1e-5
+
+
 @pytest.fixture(scope="module")
 def decode_weights_dev():
     w1, w2 = synth.decode_weights(0)
